@@ -1,0 +1,169 @@
+"""Top-k routed MoE forward over block-scaled FP4 weights, FP64.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+The path, step by step (the MoE expert computation named on [P2] "Context"
+-- the FP8xFP4 MegaMoE recipe (1, 1, 32) -- and on [P3] for the W4A16 form
+with K/16 E4M3 or K/32 E8M0 scales):
+
+  route    assignments a = t*k + j are grouped by expert id, stably (ties in
+           a-order); counts n_e, exclusive offsets o_e, sorted_assign and its
+           inverse slot_of;
+  FC1      G[a, :] = sum_h xhat[t, h] * W13_e[:, h]   (W13 rows: gate then up
+           in the kernel-native "w31"/"gate_up" order of [P3] module
+           constants and ``_normalize_w13_layout``; "w13"/"up_gate" order is
+           the same rows rotated by I, as in ``_prepare_w4a16_packed_weights``);
+  SwiGLU   h = silu(gate) * up, silu(z) = z / (1 + exp(-z));
+  h quant  A16: RNE to bfloat16 (one rounding from FP64);
+           A8 : per assignment, per 32 consecutive I elements, UE8M0 exponent
+                e = ceil(log2(amax / 448)) and E4M3 RNE of h / 2**e;
+  FC2      Y[a, :] = sum_i hhat[a, i] * W2_e[:, i];
+  combine  out[t] = sum_j topk_w[t, j] * Y[slot_of[t*k + j]], j ascending.
+
+All arithmetic is FP64; dequantised weights are exact.  Assignments whose
+expert id lies outside [0, E) are dropped (they contribute nothing), which
+is the documented behaviour of the library for such ids.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .formats import (
+    bf16_bits_decode,
+    dequant_fp4,
+    e4m3_decode,
+    rne_bf16,
+    rne_e4m3,
+    ue8m0_decode,
+)
+from .requant import _ceil_log2_ratio
+
+
+def route(topk_ids, E: int):
+    """Counting sort of assignments by expert.
+
+    Returns (counts [E], offsets [E+1], sorted_assign [A], slot_of [A]) as
+    int32; entries past offsets[E] in sorted_assign and slot_of of dropped
+    assignments are -1."""
+    ids = np.asarray(topk_ids, dtype=np.int64).reshape(-1)
+    A = ids.size
+    valid = (ids >= 0) & (ids < E)
+    counts = np.zeros(E, dtype=np.int64)
+    for a in range(A):
+        if valid[a]:
+            counts[ids[a]] += 1
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    for e in range(E):
+        offsets[e + 1] = offsets[e] + counts[e]
+    fill = offsets[:-1].copy()
+    sorted_assign = np.full(A, -1, dtype=np.int64)
+    slot_of = np.full(A, -1, dtype=np.int64)
+    for a in range(A):
+        if valid[a]:
+            p = fill[ids[a]]
+            fill[ids[a]] += 1
+            sorted_assign[p] = a
+            slot_of[a] = p
+    return (counts.astype(np.int32), offsets.astype(np.int32),
+            sorted_assign.astype(np.int32), slot_of.astype(np.int32))
+
+
+def silu(z):
+    z = np.asarray(z, dtype=np.float64)
+    return z / (1.0 + np.exp(-z))
+
+
+def quantize_h_a8(h):
+    """Per row, per 32 consecutive elements: UE8M0 e = ceil(log2(amax/448))
+    (smallest e with 448 * 2**e >= amax; amax == 0 -> e = -127), clamp to
+    [-127, 127], then E4M3 RNE of h / 2**e.  Returns (hhat values FP64,
+    fp8 bytes, scale bytes)."""
+    h = np.asarray(h, dtype=np.float64)
+    n, I = h.shape
+    blk = h.reshape(n, I // 32, 32)
+    amax = np.max(np.abs(blk), axis=-1)
+    nz = amax > 0
+    e = np.where(nz, _ceil_log2_ratio(np.where(nz, amax, 1.0), 448.0), -127)
+    e = np.clip(e, -127, 127)
+    q = rne_e4m3(np.ldexp(blk, -e[..., None]))
+    hhat = np.ldexp(e4m3_decode(q), e[..., None])
+    return hhat.reshape(n, I), q.reshape(n, I), (e + 127).astype(np.uint8)
+
+
+def decode_activations(x, x_sf=None):
+    """A16: x is [T, H] bfloat16 bit patterns (uint16).  A8: x is [T, H]
+    E4M3 bytes and x_sf [T, H/32] UE8M0 bytes; value = fp8 * 2**(sf - 127)."""
+    if x_sf is None:
+        return bf16_bits_decode(x)
+    xv = e4m3_decode(x)
+    return xv * np.repeat(ue8m0_decode(x_sf), 32, axis=1)
+
+
+def moe_forward(x, topk_ids, topk_w, w13, w13_sf, w13_gs, w2, w2_sf, w2_gs,
+                gran: int, x_sf=None, w13_order: str = "gate_up",
+                tokens=None, out_cols=None, return_parts=False):
+    """FP64 MoE forward.  Shapes: x [T, H] (see decode_activations),
+    topk_ids/topk_w [T, k], w13 [E, 2I, H/2], w13_sf [E, 2I, H/gran],
+    w2 [E, H, I/2], w2_sf [E, H, I/gran], gs [E] float32 or None.
+
+    gran 16 -> E4M3 block scales, gran 32 -> UE8M0 block scales.
+    x_sf given -> A8 activations, and h is quantised to FP8 + UE8M0 per 32;
+    otherwise A16 (bfloat16 x, bfloat16 h).
+
+    ``tokens`` / ``out_cols`` restrict the computation to a subset of output
+    rows / columns (each output element is computed by the same definition);
+    the result is then [len(tokens), len(out_cols)].
+    """
+    ids = np.asarray(topk_ids, dtype=np.int64)
+    w = np.asarray(topk_w, dtype=np.float32).astype(np.float64)
+    T, k = ids.shape
+    E, two_i, _ = np.asarray(w13).shape
+    I = two_i // 2
+    H = np.asarray(w2).shape[1]
+    kind = {16: "e4m3", 32: "ue8m0"}[gran]
+    a8 = x_sf is not None
+    tokens = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    out_cols = np.arange(H) if out_cols is None else np.asarray(out_cols, dtype=np.int64)
+
+    counts, offsets, sorted_assign, slot_of = route(ids, E)
+    xv = decode_activations(x, x_sf)
+    want = np.zeros(T * k, dtype=bool)
+    for t in tokens:
+        want[t * k:(t + 1) * k] = True
+
+    Y = {}  # slot -> FP64 row over out_cols
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        assigns = [int(a) for a in sorted_assign[lo:hi] if want[a]]
+        if not assigns:
+            continue
+        tok = np.array([a // k for a in assigns])
+        X = xv[tok]
+        gs1 = None if w13_gs is None else np.asarray(w13_gs, dtype=np.float32)[e]
+        gs2 = None if w2_gs is None else np.asarray(w2_gs, dtype=np.float32)[e]
+        W13 = dequant_fp4(w13[e], w13_sf[e], gran, kind, gs1)
+        G = X @ W13.T
+        if w13_order == "gate_up":
+            gate, up = G[:, :I], G[:, I:]
+        elif w13_order == "up_gate":
+            up, gate = G[:, :I], G[:, I:]
+        else:
+            raise ValueError(w13_order)
+        h = silu(gate) * up
+        hhat = quantize_h_a8(h)[0] if a8 else rne_bf16(h)
+        W2 = dequant_fp4(np.asarray(w2[e])[out_cols], np.asarray(w2_sf[e])[out_cols],
+                         gran, kind, gs2)
+        Ye = hhat @ W2.T
+        for r, a in enumerate(assigns):
+            Y[int(slot_of[a])] = Ye[r]
+
+    out = np.zeros((len(tokens), len(out_cols)), dtype=np.float64)
+    for r, t in enumerate(tokens):
+        for j in range(k):
+            s = int(slot_of[t * k + j])
+            if s >= 0:
+                out[r] += w[t, j] * Y[s]
+    if return_parts:
+        return out, (counts, offsets, sorted_assign, slot_of)
+    return out

@@ -1,0 +1,123 @@
+"""Pins of the oracle's group16 -> group32 requantisation: hand-derived
+blocks (golden), exactness of the scale choice, brute-force nearest codes,
+losslessness on group32-representable input, value idempotence."""
+
+import os
+
+import numpy as np
+
+import oracle
+from oracle.formats import E2M1_VALUES
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden_blocks():
+    out = []
+    with open(os.path.join(GOLDEN, "requant_blocks.txt")) as f:
+        for ln in f:
+            ln = ln.split("#")[0].strip()
+            if not ln:
+                continue
+            name, gs, s, src, exp, byte = [x.strip() for x in ln.split("|")]
+            gsv = np.array([int(gs, 16)], dtype=np.uint32).view(np.float32)
+            sf = np.array([int(v, 16) for v in s.split()], dtype=np.uint8)
+            src_c = np.array([int(c, 16) for c in src], dtype=np.uint8)
+            exp_c = np.array([int(c, 16) for c in exp], dtype=np.uint8)
+            out.append((name, gsv, sf, src_c, exp_c, int(byte)))
+    return out
+
+
+def test_golden_blocks():
+    blocks = _golden_blocks()
+    assert len(blocks) >= 10
+    for name, gs, sf, src, exp, byte in blocks:
+        packed = oracle.pack_fp4(src)[None, None, :]
+        dst, dsf = oracle.requant_g16_to_g32(packed, sf[None, None, :], gs)
+        assert np.array_equal(oracle.unpack_fp4(dst[0, 0]), exp), name
+        assert int(dsf[0, 0, 0]) == byte, name
+
+
+def _random_g16(rng, E, N, K, lo=-10.0, hi=-3.0):
+    import torch
+    src = rng.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
+    s = np.exp2(rng.uniform(lo, hi, size=(E, N, K // 16))).astype(np.float32)
+    sf = torch.from_numpy(s).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    gs = rng.uniform(0.5, 2.0, size=E).astype(np.float32)
+    return src, sf, gs
+
+
+def test_brute_force_scale_and_codes():
+    """Every block: e is the smallest integer with 6*2**e >= amax, and every
+    code is the nearest E2M1 grid point times 2**e (ties to even code), with
+    the sign of the source value."""
+    rng = np.random.default_rng(10)
+    src, sf, gs = _random_g16(rng, 3, 8, 256)
+    dst, dsf = oracle.requant_g16_to_g32(src, sf, gs)
+    for e in range(3):
+        v = oracle.dequant_fp4(src[e], sf[e], 16, "e4m3", gs[e])
+        codes = oracle.unpack_fp4(dst[e])
+        for n in range(8):
+            for b in range(256 // 32):
+                blk = v[n, 32 * b:32 * b + 32]
+                amax = float(np.max(np.abs(blk)))
+                ex = int(dsf[e, n, b]) - 127
+                assert 6.0 * 2.0 ** ex >= amax and 6.0 * 2.0 ** (ex - 1) < amax
+                for i, val in enumerate(blk):
+                    c = int(codes[n, 32 * b + i])
+                    grid = E2M1_VALUES * 2.0 ** ex
+                    d = np.abs(grid - abs(val))
+                    cand = np.flatnonzero(d == d.min())
+                    want = cand[0] if len(cand) == 1 else [x for x in cand if x % 2 == 0][0]
+                    assert (c & 7) == want
+                    assert (c >> 3) == int(np.signbit(val))
+
+
+def test_lossless_on_g32_representable_input():
+    """A group16 tensor whose two half-block scales are the same power of two
+    (gs = 1) is group32-representable: requant must restore it exactly."""
+    rng = np.random.default_rng(11)
+    E, N, K = 2, 16, 512
+    src = rng.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
+    ex = rng.integers(-9, 9, size=(E, N, K // 32))
+    # E4M3 bytes of 2**ex: normal for ex >= -6 (exponent field ex + 7), subnormal below
+    byte = np.where(ex >= -6, (ex + 7) << 3, 1 << (ex + 9)).astype(np.uint8)
+    sf = np.repeat(byte, 2, axis=2)
+    assert np.array_equal(oracle.e4m3_decode(sf), np.repeat(2.0 ** ex, 2, axis=2))
+    ones = np.ones(E, np.float32)
+    dst, dsf = oracle.requant_g16_to_g32(src, sf, ones)
+    for e in range(E):
+        a = oracle.dequant_fp4(src[e], sf[e], 16, "e4m3", 1.0)
+        b = oracle.dequant_fp4(dst[e], dsf[e], 32, "ue8m0")
+        assert np.array_equal(a, b)
+
+
+def test_value_idempotence():
+    """dequant(requant(dequant(requant(x)))) == dequant(requant(x)) exactly;
+    the group32 result is fed back as group16 with both half scales equal to
+    its UE8M0 scale (shifted into E4M3 range by a power-of-two global)."""
+    rng = np.random.default_rng(12)
+    src, sf, gs = _random_g16(rng, 2, 16, 512)
+    d1, s1 = oracle.requant_g16_to_g32(src, sf, gs)
+    shift = 6
+    ex = s1.astype(np.int64) - 127 + shift
+    assert ex.min() >= -6 and ex.max() <= 8
+    sf2 = np.repeat(((ex + 7) << 3).astype(np.uint8), 2, axis=2)
+    gs2 = np.full(2, 2.0 ** -shift, np.float32)
+    d2, s2 = oracle.requant_g16_to_g32(d1, sf2, gs2)
+    for e in range(2):
+        a = oracle.dequant_fp4(d1[e], s1[e], 32, "ue8m0")
+        b = oracle.dequant_fp4(d2[e], s2[e], 32, "ue8m0")
+        assert np.array_equal(a, b)
+
+
+def test_error_bound():
+    """Requantisation error of each element is at most half the E2M1 grid
+    step at its magnitude times 2**e, i.e. <= 2**e (step 2 near 6)."""
+    rng = np.random.default_rng(13)
+    src, sf, gs = _random_g16(rng, 1, 32, 1024)
+    d, s = oracle.requant_g16_to_g32(src, sf, gs)
+    a = oracle.dequant_fp4(src[0], sf[0], 16, "e4m3", gs[0]).reshape(32, 32, 32)
+    b = oracle.dequant_fp4(d[0], s[0], 32, "ue8m0").reshape(32, 32, 32)
+    step = 2.0 ** (s[0].astype(np.int64) - 127)[..., None]
+    assert np.all(np.abs(a - b) <= step * 1.0)
