@@ -1,0 +1,201 @@
+"""block_scaled_fp4_topk_amd -- Python binding of libmoefp4 (MI355X / gfx950).
+
+Thin ctypes marshalling over the C ABI declared in ``include/moefp4.h``:
+every step of the MoE forward and of the requantisation runs in the HIP
+kernels of the library.  PyTorch only provides device memory and the current
+stream.  There is no CPU fallback: if ``libmoefp4.so`` is missing or no GPU is
+present the calls raise.
+
+Functions mirror the C entry points:
+  workspace_bytes(problem)            -> moe_fp4_workspace_bytes
+  route(problem, topk_ids, ...)       -> moe_fp4_route
+  forward(x, topk_ids, topk_w, ...)   -> moe_fp4_forward
+  requant_gran_k(src, src_sf, ...)    -> fp4_requant_gran_k
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["Problem", "MoeFp4Error", "lib", "workspace_bytes", "route", "forward",
+           "requant_gran_k", "dropped_assignments", "LIB_PATH"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoefp4.so")
+
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = range(5)
+ACT_BF16, ACT_FP8_UE8M0_K32 = 0, 1
+GATE_UP, UP_GATE = 0, 1
+
+
+OUT_BF16, OUT_F32 = 0, 1
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("T", "E", "top_k", "H", "I", "gran_k", "act_fmt", "w13_order", "out_fmt")]
+
+
+class MoeFp4Error(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"moefp4 status {status}: {message}")
+        self.status = status
+
+
+_lib = None
+_P = ctypes.c_void_p
+
+
+def lib():
+    """Load libmoefp4.so (built in-tree by ``python -m block_scaled_fp4_topk_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run python -m block_scaled_fp4_topk_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        st = ctypes.c_int
+        L.moe_fp4_workspace_bytes.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(ctypes.c_size_t)]
+        L.moe_fp4_workspace_bytes.restype = st
+        L.moe_fp4_route.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+        L.moe_fp4_route.restype = st
+        L.moe_fp4_forward.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                      _P, _P, ctypes.c_size_t, _P]
+        L.moe_fp4_forward.restype = st
+        L.fp4_requant_gran_k.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _P, _P,
+                                         ctypes.c_int32, _P, _P, _P, ctypes.c_int32, _P]
+        L.fp4_requant_gran_k.restype = st
+        L.moefp4_last_error.argtypes = []
+        L.moefp4_last_error.restype = ctypes.c_char_p
+        L.moefp4_version.argtypes = []
+        L.moefp4_version.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != OK:
+        raise MoeFp4Error(status, lib().moefp4_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(t, name, dtypes):
+    import torch
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} must have dtype in {dtypes}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def make_problem(T, E, top_k, H, I, gran_k, act_fmt=ACT_BF16, w13_order=GATE_UP,
+                 out_fmt=OUT_BF16) -> Problem:
+    if isinstance(w13_order, str):
+        w13_order = {"gate_up": GATE_UP, "w31": GATE_UP, "up_gate": UP_GATE, "w13": UP_GATE}[w13_order]
+    return Problem(T, E, top_k, H, I, gran_k, act_fmt, w13_order, out_fmt)
+
+
+def workspace_bytes(problem: Problem) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().moe_fp4_workspace_bytes(ctypes.byref(problem), ctypes.byref(n)))
+    return n.value
+
+
+def _workspace(problem, workspace, device):
+    import torch
+    need = workspace_bytes(problem)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    return workspace
+
+
+def route(problem: Problem, topk_ids, workspace=None, stream=None):
+    """Returns (counts [E], offsets [E+1], sorted_assign [T*k], slot_of [T*k]) int32 tensors."""
+    import torch
+    _dev(topk_ids, "topk_ids", (torch.int32,))
+    dev = topk_ids.device
+    A = problem.T * problem.top_k
+    counts = torch.empty(problem.E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(problem.E + 1, dtype=torch.int32, device=dev)
+    sa = torch.empty(max(A, 1), dtype=torch.int32, device=dev)
+    so = torch.empty(max(A, 1), dtype=torch.int32, device=dev)
+    ws = _workspace(problem, workspace, dev)
+    _check(lib().moe_fp4_route(ctypes.byref(problem), _ptr(topk_ids), _ptr(counts), _ptr(offsets),
+                               _ptr(sa), _ptr(so), _ptr(ws), ws.numel(), _stream(stream)))
+    return counts, offsets, sa[:A], so[:A]
+
+
+def forward(x, topk_ids, topk_w, w13, w13_sf, w13_gs, w2, w2_sf, w2_gs, gran_k, x_sf=None,
+            w13_order="gate_up", out=None, workspace=None, stream=None, out_dtype=None):
+    """MoE forward on the GPU.  x: [T, H] bfloat16 (A16) or uint8/float8_e4m3fn
+    with x_sf [T, H/32] uint8 (A8).  Weights uint8 as in include/moefp4.h.
+    Returns out [T, H] bfloat16 (default) or float32 (out_dtype=torch.float32)."""
+    import torch
+    u8 = (torch.uint8,)
+    fp8 = (torch.uint8, torch.float8_e4m3fn)
+    a8 = x_sf is not None
+    _dev(x, "x", fp8 if a8 else (torch.bfloat16, torch.int16, torch.uint16))
+    _dev(x_sf, "x_sf", u8)
+    _dev(topk_ids, "topk_ids", (torch.int32,))
+    _dev(topk_w, "topk_w", (torch.float32,))
+    for n, t in (("w13", w13), ("w13_sf", w13_sf), ("w2", w2), ("w2_sf", w2_sf)):
+        _dev(t, n, u8)
+    _dev(w13_gs, "w13_gs", (torch.float32,))
+    _dev(w2_gs, "w2_gs", (torch.float32,))
+    T, H = x.shape
+    E, two_i, _ = w13.shape
+    k = topk_ids.shape[1]
+    if out_dtype is None:
+        out_dtype = torch.bfloat16 if out is None else out.dtype
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out_dtype must be torch.bfloat16 or torch.float32")
+    p = make_problem(T, E, k, H, two_i // 2, gran_k, ACT_FP8_UE8M0_K32 if a8 else ACT_BF16, w13_order,
+                     OUT_F32 if out_dtype == torch.float32 else OUT_BF16)
+    if out is None:
+        out = torch.empty((T, H), dtype=out_dtype, device=x.device)
+    _dev(out, "out", (out_dtype,))
+    ws = _workspace(p, workspace, x.device)
+    _check(lib().moe_fp4_forward(ctypes.byref(p), _ptr(x), _ptr(x_sf), _ptr(topk_ids), _ptr(topk_w),
+                                 _ptr(w13), _ptr(w13_sf), _ptr(w13_gs), _ptr(w2), _ptr(w2_sf),
+                                 _ptr(w2_gs), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def requant_gran_k(src, src_sf, src_gs=None, src_gran=16, dst_gran=32, dst=None, dst_sf=None,
+                   stream=None):
+    """Group16 -> group32 requantisation.  src [E, N, K/2] uint8, src_sf
+    [E, N, K/16] uint8 (E4M3), src_gs [E] float32 or None.  Returns
+    (dst [E, N, K/2], dst_sf [E, N, K/32]); dst may be src (in place)."""
+    import torch
+    _dev(src, "src", (torch.uint8,))
+    _dev(src_sf, "src_sf", (torch.uint8,))
+    _dev(src_gs, "src_gs", (torch.float32,))
+    E, N, kh = src.shape
+    K = 2 * kh
+    if dst is None:
+        dst = torch.empty_like(src)
+    if dst_sf is None:
+        dst_sf = torch.empty((E, N, K // dst_gran), dtype=torch.uint8, device=src.device)
+    _dev(dst, "dst", (torch.uint8,))
+    _dev(dst_sf, "dst_sf", (torch.uint8,))
+    _check(lib().fp4_requant_gran_k(E, N, K, _ptr(src), _ptr(src_sf), src_gran, _ptr(src_gs),
+                                    _ptr(dst), _ptr(dst_sf), dst_gran, _stream(stream)))
+    return dst, dst_sf
+
+
+def dropped_assignments(workspace) -> int:
+    """Number of assignments with an expert id outside [0, E) in the last
+    route / forward call that used ``workspace`` (synchronises)."""
+    return int(workspace[:4].view(dtype=__import__("torch").int32).item())

@@ -1,0 +1,300 @@
+// C-ABI entry points of libmoefp4: argument validation, workspace planning
+// and the launch sequence on the caller's stream.  No allocation, no
+// synchronisation; every check runs before the first launch.
+#include <hip/hip_runtime.h>
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "../../include/moefp4.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+moefp4_status fail(moefp4_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+moefp4_status ok() {
+  g_err.clear();
+  return MOEFP4_OK;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Layout {
+  size_t flags, counts, offsets, sorted, slot_of, tiles, ntiles;
+  size_t act_scale, x16, hmax, h, h_sf, y, total;
+  int tile_m, nt, max_tiles;
+  bool a8, g16_a16;
+};
+
+moefp4_status check_problem(const moefp4_problem* p) {
+  if (!p) return fail(MOEFP4_EINVAL, "problem is NULL");
+  if (p->T < 0) return fail(MOEFP4_EINVAL, "T must be >= 0, got %d", p->T);
+  if (p->E < 1 || p->E > moefp4::kMaxExperts)
+    return fail(p->E < 1 ? MOEFP4_EINVAL : MOEFP4_EUNSUPPORTED, "E must be in [1, %d], got %d",
+                moefp4::kMaxExperts, p->E);
+  if (p->top_k < 1 || p->top_k > p->E)
+    return fail(MOEFP4_EINVAL, "top_k must be in [1, E=%d], got %d", p->E, p->top_k);
+  if (p->H <= 0 || p->I <= 0) return fail(MOEFP4_EINVAL, "H and I must be positive");
+  if (p->gran_k != 16 && p->gran_k != 32)
+    return fail(MOEFP4_EINVAL, "gran_k must be 16 or 32, got %d", p->gran_k);
+  if (p->act_fmt != MOEFP4_ACT_BF16 && p->act_fmt != MOEFP4_ACT_FP8_UE8M0_K32)
+    return fail(MOEFP4_EINVAL, "unknown act_fmt %d", p->act_fmt);
+  if (p->w13_order != MOEFP4_GATE_UP && p->w13_order != MOEFP4_UP_GATE)
+    return fail(MOEFP4_EINVAL, "unknown w13_order %d", p->w13_order);
+  if (p->out_fmt != MOEFP4_OUT_BF16 && p->out_fmt != MOEFP4_OUT_F32)
+    return fail(MOEFP4_EINVAL, "unknown out_fmt %d", p->out_fmt);
+  if (p->H % 32 || p->I % 32)
+    return fail(MOEFP4_EINVAL, "H and I must be multiples of 32 (K blocks of the scale grid), got H=%d I=%d",
+                p->H, p->I);
+  if (p->act_fmt == MOEFP4_ACT_FP8_UE8M0_K32 && p->gran_k == 16)
+    return fail(MOEFP4_EUNSUPPORTED,
+                "FP8 activations with group16 weights (recipe (1,1,16)) are not computed: requantise the "
+                "weights to group32 with fp4_requant_gran_k");
+  if (p->H % 256 || p->I % 256)
+    return fail(MOEFP4_EUNSUPPORTED, "this build tiles K in chunks of 256: H and I must be multiples of 256, got H=%d I=%d",
+                p->H, p->I);
+  const long long A = (long long)p->T * p->top_k;
+  if (A > (1LL << 26)) return fail(MOEFP4_EUNSUPPORTED, "T*top_k = %lld exceeds 2^26", A);
+  return MOEFP4_OK;
+}
+
+moefp4_status plan(const moefp4_problem* p, Layout* L) {
+  moefp4_status st = check_problem(p);
+  if (st != MOEFP4_OK) return st;
+  const size_t A = (size_t)p->T * p->top_k, E = p->E, T = p->T, H = p->H, I = p->I;
+  L->a8 = p->act_fmt == MOEFP4_ACT_FP8_UE8M0_K32;
+  L->g16_a16 = !L->a8 && p->gran_k == 16;
+  const size_t active = A < E ? A : E;
+  const double avg = active ? (double)A / (double)active : 0.0;
+  L->nt = avg > 16.0 ? 4 : 1;
+  L->tile_m = 16 * L->nt;
+  L->max_tiles = (int)(A / L->tile_m + active);
+  size_t o = 0;
+  auto take = [&](size_t bytes) { const size_t at = o; o = align_up(o + bytes); return at; };
+  L->flags = take(64);
+  L->counts = take(E * 4);
+  L->offsets = take((E + 1) * 4);
+  L->sorted = take(A * 4);
+  L->slot_of = take(A * 4);
+  L->tiles = take((size_t)L->max_tiles * 8);
+  L->ntiles = take(4);
+  L->act_scale = take(L->g16_a16 ? T * 4 : 0);
+  L->x16 = take(L->g16_a16 ? T * H * 2 : 0);
+  L->hmax = take(L->g16_a16 ? A * 4 : 0);
+  L->h = take(L->a8 ? A * I : A * I * 2);
+  L->h_sf = take(L->a8 ? A * (I / 32) : 0);
+  L->y = take(A * H * 4);
+  L->total = o;
+  return MOEFP4_OK;
+}
+
+template <class T>
+T* at(void* base, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(base) + off);
+}
+
+bool misaligned(const void* p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a != 0; }
+
+moefp4_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MOEFP4_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return MOEFP4_OK;
+}
+
+moefp4_status route_into(const moefp4_problem* p, const Layout& L, const int32_t* ids,
+                         int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* slot_of,
+                         void* ws, uint32_t* zero_words, int n_zero, hipStream_t s) {
+  moefp4::RouteOut o;
+  o.counts = counts;
+  o.offsets = offsets;
+  o.sorted_assign = sorted;
+  o.slot_of = slot_of;
+  o.tiles = at<int32_t>(ws, L.tiles);
+  o.ntiles = at<int32_t>(ws, L.ntiles);
+  o.flags = at<int32_t>(ws, L.flags);
+  o.zero_words = zero_words;
+  o.n_zero = n_zero;
+  return hip_status(moefp4::launch_route(ids, p->T * p->top_k, p->E, L.tile_m, o, s), "route");
+}
+
+}  // namespace
+
+extern "C" {
+
+moefp4_status moe_fp4_workspace_bytes(const moefp4_problem* p, size_t* bytes) {
+  if (!bytes) return fail(MOEFP4_EINVAL, "bytes is NULL");
+  Layout L;
+  moefp4_status st = plan(p, &L);
+  if (st != MOEFP4_OK) return st;
+  *bytes = L.total;
+  return ok();
+}
+
+moefp4_status moe_fp4_route(const moefp4_problem* p, const int32_t* topk_ids, int32_t* counts,
+                            int32_t* offsets, int32_t* sorted_assign, int32_t* slot_of,
+                            void* workspace, size_t ws_bytes, hipStream_t stream) {
+  Layout L;
+  moefp4_status st = plan(p, &L);
+  if (st != MOEFP4_OK) return st;
+  if (p->T > 0 && (!topk_ids || !sorted_assign || !slot_of))
+    return fail(MOEFP4_EINVAL, "topk_ids, sorted_assign and slot_of must be non-NULL");
+  if (!counts || !offsets) return fail(MOEFP4_EINVAL, "counts and offsets must be non-NULL");
+  if (!workspace || ws_bytes < L.total)
+    return fail(MOEFP4_EWORKSPACE, "workspace of %zu bytes needed, got %zu", L.total,
+                workspace ? ws_bytes : (size_t)0);
+  st = route_into(p, L, topk_ids, counts, offsets, sorted_assign, slot_of, workspace, nullptr, 0,
+                  stream);
+  return st == MOEFP4_OK ? ok() : st;
+}
+
+moefp4_status moe_fp4_forward(const moefp4_problem* p, const void* x, const uint8_t* x_sf,
+                              const int32_t* topk_ids, const float* topk_w, const uint8_t* w13,
+                              const uint8_t* w13_sf, const float* w13_gs, const uint8_t* w2,
+                              const uint8_t* w2_sf, const float* w2_gs, void* out,
+                              void* workspace, size_t ws_bytes, hipStream_t stream) {
+  Layout L;
+  moefp4_status st = plan(p, &L);
+  if (st != MOEFP4_OK) return st;
+  if (p->T == 0) return ok();
+  if (!x || !topk_ids || !topk_w || !w13 || !w13_sf || !w2 || !w2_sf || !out)
+    return fail(MOEFP4_EINVAL, "x, topk_ids, topk_w, w13, w13_sf, w2, w2_sf and out must be non-NULL");
+  if (L.a8 && !x_sf) return fail(MOEFP4_EINVAL, "FP8 activations need x_sf");
+  if (!L.a8 && x_sf) return fail(MOEFP4_EINVAL, "x_sf must be NULL for bfloat16 activations");
+  if (misaligned(x, 16) || misaligned(w13, 16) || misaligned(w2, 16) || misaligned(out, 16) ||
+      misaligned(w13_sf, 8) || misaligned(w2_sf, 8) || (x_sf && misaligned(x_sf, 8)))
+    return fail(MOEFP4_EINVAL, "x, w13, w2, out must be 16-byte aligned; scale tensors 8-byte aligned");
+  if (!workspace || ws_bytes < L.total)
+    return fail(MOEFP4_EWORKSPACE, "workspace of %zu bytes needed, got %zu", L.total,
+                workspace ? ws_bytes : (size_t)0);
+  if (misaligned(workspace, 256)) return fail(MOEFP4_EINVAL, "workspace must be 256-byte aligned");
+
+  const int A = p->T * p->top_k;
+  int32_t* counts = at<int32_t>(workspace, L.counts);
+  int32_t* offsets = at<int32_t>(workspace, L.offsets);
+  int32_t* sorted = at<int32_t>(workspace, L.sorted);
+  int32_t* slot_of = at<int32_t>(workspace, L.slot_of);
+  uint32_t* hmax = L.g16_a16 ? at<uint32_t>(workspace, L.hmax) : nullptr;
+  st = route_into(p, L, topk_ids, counts, offsets, sorted, slot_of, workspace, hmax,
+                  L.g16_a16 ? A : 0, stream);
+  if (st != MOEFP4_OK) return st;
+
+  moefp4::FcArgs a;
+  memset(&a, 0, sizeof a);
+  a.tiles = at<int32_t>(workspace, L.tiles);
+  a.ntiles = at<int32_t>(workspace, L.ntiles);
+  a.counts = counts;
+  a.offsets = offsets;
+  a.sorted_assign = sorted;
+  a.I = p->I;
+  a.H = p->H;
+  a.top_k = p->top_k;
+  a.w13_order = p->w13_order;
+
+  // FC1 + SwiGLU (+ h quantisation)
+  a.w = w13;
+  a.wsf = w13_sf;
+  a.gs = w13_gs;
+  a.K = p->H;
+  a.N = 2 * p->I;
+  a.h_out = at<void>(workspace, L.h);
+  if (L.a8) {
+    a.act = x;
+    a.act_sf = x_sf;
+    a.h_sf_out = at<uint8_t>(workspace, L.h_sf);
+    st = hip_status(moefp4::launch_fc1_a8(a, L.nt, L.max_tiles, stream), "fc1");
+  } else {
+    if (L.g16_a16) {
+      uint16_t* x16 = at<uint16_t>(workspace, L.x16);
+      float* xs = at<float>(workspace, L.act_scale);
+      st = hip_status(moefp4::launch_rows_to_f16(static_cast<const uint16_t*>(x), p->T, p->H, x16, xs,
+                                                 stream),
+                      "rows_to_f16");
+      if (st != MOEFP4_OK) return st;
+      a.act = x16;
+      a.act_scale = xs;
+      a.hmax_out = hmax;
+    } else {
+      a.act = x;
+    }
+    st = hip_status(moefp4::launch_fc1_a16(a, p->gran_k, L.nt, L.max_tiles, stream), "fc1");
+  }
+  if (st != MOEFP4_OK) return st;
+
+  // FC2
+  a.w = w2;
+  a.wsf = w2_sf;
+  a.gs = w2_gs;
+  a.K = p->I;
+  a.N = p->H;
+  a.act = at<void>(workspace, L.h);
+  a.act_sf = L.a8 ? at<uint8_t>(workspace, L.h_sf) : nullptr;
+  a.act_scale = nullptr;
+  a.hmax_in = hmax;
+  a.hmax_out = nullptr;
+  a.h_out = nullptr;
+  a.h_sf_out = nullptr;
+  a.y_out = at<float>(workspace, L.y);
+  st = hip_status(L.a8 ? moefp4::launch_fc2_a8(a, L.nt, L.max_tiles, stream)
+                       : moefp4::launch_fc2_a16(a, p->gran_k, L.nt, L.max_tiles, stream),
+                  "fc2");
+  if (st != MOEFP4_OK) return st;
+
+  st = hip_status(moefp4::launch_combine(a.y_out, slot_of, topk_w, p->T, p->top_k, p->H, out,
+                                         p->out_fmt == MOEFP4_OUT_F32, stream),
+                  "combine");
+  return st == MOEFP4_OK ? ok() : st;
+}
+
+moefp4_status fp4_requant_gran_k(int64_t E, int64_t N, int64_t K, const uint8_t* src,
+                                 const uint8_t* src_sf, int32_t src_gran, const float* src_gs,
+                                 uint8_t* dst, uint8_t* dst_sf, int32_t dst_gran,
+                                 hipStream_t stream) {
+  if (E < 0 || N < 0 || K < 0) return fail(MOEFP4_EINVAL, "E, N, K must be >= 0");
+  if ((src_gran != 16 && src_gran != 32) || (dst_gran != 16 && dst_gran != 32))
+    return fail(MOEFP4_EINVAL, "granularities must be 16 or 32, got %d -> %d", src_gran, dst_gran);
+  if (src_gran != 16 || dst_gran != 32)
+    return fail(MOEFP4_EUNSUPPORTED, "only group16 -> group32 requantisation is computed, got %d -> %d",
+                src_gran, dst_gran);
+  if (K % 32) return fail(MOEFP4_EINVAL, "K must be a multiple of 32, got %lld", (long long)K);
+  const int64_t n = E * N * K;
+  if (n == 0) return ok();
+  if (!src || !src_sf || !dst || !dst_sf)
+    return fail(MOEFP4_EINVAL, "src, src_sf, dst and dst_sf must be non-NULL");
+  if (misaligned(src, 16) || misaligned(dst, 16) || misaligned(src_sf, 8) || misaligned(dst_sf, 4))
+    return fail(MOEFP4_EINVAL, "src/dst must be 16-byte aligned, src_sf 8-byte, dst_sf 4-byte");
+  // overlap rules: dst == src allowed; everything else disjoint
+  struct R { uintptr_t b, e; } r[4] = {
+      {(uintptr_t)src, (uintptr_t)src + (uintptr_t)(n / 2)},
+      {(uintptr_t)src_sf, (uintptr_t)src_sf + (uintptr_t)(n / 16)},
+      {(uintptr_t)dst, (uintptr_t)dst + (uintptr_t)(n / 2)},
+      {(uintptr_t)dst_sf, (uintptr_t)dst_sf + (uintptr_t)(n / 32)}};
+  for (int i = 0; i < 4; ++i)
+    for (int j = i + 1; j < 4; ++j) {
+      if (i == 0 && j == 2 && src == dst) continue;
+      if (r[i].b < r[j].e && r[j].b < r[i].e)
+        return fail(MOEFP4_EINVAL, "buffers overlap (only dst == src is allowed)");
+    }
+  moefp4_status st = hip_status(
+      moefp4::launch_requant_g16_g32(src, src_sf, src_gs, dst, dst_sf, E, N, K, stream), "requant");
+  return st == MOEFP4_OK ? ok() : st;
+}
+
+const char* moefp4_last_error(void) { return g_err.c_str(); }
+
+const char* moefp4_version(void) { return "moefp4 0.1 gfx950"; }
+
+}  // extern "C"

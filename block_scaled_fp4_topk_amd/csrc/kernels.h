@@ -1,0 +1,67 @@
+// Internal launcher interface between the C-ABI layer (api.cpp) and the HIP
+// kernels.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moefp4 {
+
+constexpr int kMaxExperts = 512;
+
+// Tile of activation rows processed by one grouped-GEMM workgroup.
+struct RouteOut {
+  int32_t* counts;         // [E]
+  int32_t* offsets;        // [E+1]
+  int32_t* sorted_assign;  // [A]
+  int32_t* slot_of;        // [A]
+  int32_t* tiles;          // [2 * max_tiles] (expert, first row)
+  int32_t* ntiles;         // [1]
+  int32_t* flags;          // [1] dropped assignments
+  uint32_t* zero_words;    // optional [n_zero] words cleared by the route kernel
+  int n_zero;
+};
+
+hipError_t launch_route(const int32_t* topk_ids, int A, int E, int tile_m, const RouteOut& o,
+                        hipStream_t s);
+
+// bf16 [T, H] -> fp16 [T, H] * 2**-p_t with p_t chosen per row so the row
+// maximum lands in [2**14, 2**15); scale[t] = 2**p_t.
+hipError_t launch_rows_to_f16(const uint16_t* x, int T, int H, uint16_t* x16, float* scale,
+                              hipStream_t s);
+
+struct FcArgs {
+  const uint8_t* w;          // [E, N, K/2]
+  const uint8_t* wsf;        // [E, N, K/gran]
+  const float* gs;           // [E] or null
+  const void* act;           // FC1: x or x16 [T, K]; FC2: h [A, K]
+  const uint8_t* act_sf;     // A8: [rows, K/32] UE8M0
+  const float* act_scale;    // A16 group16 FC1: per token 2**p
+  const uint32_t* hmax_in;   // A16 group16 FC2: per slot max |h| bits
+  const int32_t* tiles;
+  const int32_t* ntiles;
+  const int32_t* counts;
+  const int32_t* offsets;
+  const int32_t* sorted_assign;
+  int K, N, I, H, top_k, w13_order;
+  void* h_out;               // FC1: h [A, I] (bf16 or fp8)
+  uint8_t* h_sf_out;         // FC1 A8: [A, I/32]
+  uint32_t* hmax_out;        // FC1 A16 group16: per slot max |h| bits
+  float* y_out;              // FC2: [A, H]
+};
+
+hipError_t launch_fc1_a16(const FcArgs& a, int gran, int nt, int max_tiles, hipStream_t s);
+hipError_t launch_fc2_a16(const FcArgs& a, int gran, int nt, int max_tiles, hipStream_t s);
+hipError_t launch_fc1_a8(const FcArgs& a, int nt, int max_tiles, hipStream_t s);
+hipError_t launch_fc2_a8(const FcArgs& a, int nt, int max_tiles, hipStream_t s);
+
+// out[t, :] = sum_j w[t, j] * y[slot_of[t*k + j], :]  (f32, or rounded to bf16)
+hipError_t launch_combine(const float* y, const int32_t* slot_of, const float* topk_w, int T,
+                          int k, int H, void* out, bool out_f32, hipStream_t s);
+
+hipError_t launch_requant_g16_g32(const uint8_t* src, const uint8_t* src_sf, const float* gs,
+                                  uint8_t* dst, uint8_t* dst_sf, int64_t E, int64_t N, int64_t K,
+                                  hipStream_t s);
+
+}  // namespace moefp4

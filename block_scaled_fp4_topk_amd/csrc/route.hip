@@ -1,0 +1,185 @@
+// Routing: stable counting sort of the T*k assignments by expert id, the
+// per-expert tile list of the grouped GEMMs, and the fp16 row preparation
+// used by the group16 (E4M3-scaled) path.
+//
+// The grouping is the "top-k routed tokens gathered per expert" step of the
+// fused MoE (GLM-5.2 NVFP4 group16 MegaMoE notes, Context; b12x W4A16
+// prepare.py, make_w4a16_packed_buffers sizes its buffers by tokens and
+// top-k).  The order inside an expert is the assignment order a = t*k + j,
+// made deterministic without atomics on positions: within a wavefront the
+// rank of a lane among lanes with the same expert comes from ballots over
+// the bits of the expert id; across wavefronts from per-wave counts in LDS.
+#include "common.h"
+#include "kernels.h"
+
+namespace moefp4 {
+
+namespace {
+
+constexpr int kRouteThreads = 1024;
+constexpr int kRouteWaves = kRouteThreads / 64;
+
+// Exclusive scan of v over the whole block (one value per thread);
+// returns the exclusive prefix, *total gets the block sum.
+__device__ int block_exclusive_scan(int v, int* s_tmp, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) s_tmp[wave] = x;
+  __syncthreads();
+  if (wave == 0) {
+    int w = lane < kRouteWaves ? s_tmp[lane] : 0;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      int y = __shfl_up(w, d, 64);
+      if (lane >= d) w += y;
+    }
+    if (lane < kRouteWaves) s_tmp[64 + lane] = w;  // inclusive wave prefix
+  }
+  __syncthreads();
+  const int before = wave ? s_tmp[64 + wave - 1] : 0;
+  *total = s_tmp[64 + kRouteWaves - 1];
+  __syncthreads();
+  return before + x - v;
+}
+
+__global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t* __restrict__ ids,
+                                                              int A, int E, int tile_m,
+                                                              RouteOut o) {
+  extern __shared__ int smem[];
+  int* s_base = smem;                 // [E] running start of each expert
+  int* s_wc = s_base + E;             // [kRouteWaves][E] per-wave counts of a chunk
+  __shared__ int s_cnt[kMaxExperts];
+  __shared__ int s_tmp[128];
+  __shared__ int s_drop;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  for (int i = tid; i < o.n_zero; i += kRouteThreads) o.zero_words[i] = 0u;
+  for (int e = tid; e < E; e += kRouteThreads) s_cnt[e] = 0;
+  if (tid == 0) s_drop = 0;
+  __syncthreads();
+
+  // 1. histogram (LDS atomics: the counts do not depend on their order)
+  int drop = 0;
+  for (int a = tid; a < A; a += kRouteThreads) {
+    const int e = ids[a];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&s_cnt[e], 1);
+    else ++drop;
+  }
+  if (drop) atomicAdd(&s_drop, drop);
+  __syncthreads();
+
+  // 2. exclusive scans: expert offsets and tile offsets (E <= 1024 = threads)
+  const int c = tid < E ? s_cnt[tid] : 0;
+  int valid_total;
+  const int base = block_exclusive_scan(c, s_tmp, &valid_total);
+  const int nt = (c + tile_m - 1) / tile_m;
+  int tiles_total;
+  const int tbase = block_exclusive_scan(nt, s_tmp, &tiles_total);
+  if (tid < E) {
+    o.counts[tid] = c;
+    o.offsets[tid] = base;
+    s_base[tid] = base;
+    for (int i = 0; i < nt; ++i) {
+      o.tiles[2 * (tbase + i)] = tid;
+      o.tiles[2 * (tbase + i) + 1] = i * tile_m;
+    }
+  }
+  if (tid == 0) {
+    o.offsets[E] = valid_total;
+    o.ntiles[0] = tiles_total;
+    o.flags[0] = s_drop;
+  }
+
+  // 3. stable scatter, 1024 assignments per pass
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  for (int c0 = 0; c0 < A; c0 += kRouteThreads) {
+    for (int i = tid; i < kRouteWaves * E; i += kRouteThreads) s_wc[i] = 0;
+    const int a = c0 + tid;
+    const int e = a < A ? ids[a] : -1;
+    const bool valid = a < A && (unsigned)e < (unsigned)E;
+    uint64_t peers = ballot(valid);
+    const int key = valid ? e : 0;
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (key >> b) & 1;
+      const uint64_t m = ballot(bit);
+      peers &= bit ? m : ~m;
+    }
+    const int rank = __popcll(peers & ((1ull << lane) - 1ull));
+    __syncthreads();  // s_wc cleared
+    if (valid && rank == 0) s_wc[wave * E + e] = __popcll(peers);
+    __syncthreads();
+    if (valid) {
+      int pos = s_base[e] + rank;
+      for (int w = 0; w < wave; ++w) pos += s_wc[w * E + e];
+      o.sorted_assign[pos] = a;
+      o.slot_of[a] = pos;
+    } else if (a < A) {
+      o.slot_of[a] = -1;
+    }
+    __syncthreads();
+    for (int ee = tid; ee < E; ee += kRouteThreads) {
+      int s = 0;
+      for (int w = 0; w < kRouteWaves; ++w) s += s_wc[w * E + ee];
+      s_base[ee] += s;
+    }
+    __syncthreads();
+  }
+  for (int i = valid_total + tid; i < A; i += kRouteThreads) o.sorted_assign[i] = -1;
+}
+
+__global__ __launch_bounds__(256) void rows_to_f16_kernel(const uint16_t* __restrict__ x, int T,
+                                                          int H, uint16_t* __restrict__ x16,
+                                                          float* __restrict__ scale) {
+  __shared__ uint32_t s_max[4];
+  const int t = blockIdx.x;
+  if (t >= T) return;
+  const uint16_t* row = x + (size_t)t * H;
+  uint32_t m = 0;
+  for (int i = threadIdx.x; i < H; i += 256) {
+    const uint32_t b = (uint32_t)(row[i] & 0x7FFF) << 16;
+    m = b > m ? b : m;
+  }
+  for (int d = 32; d >= 1; d >>= 1) {
+    const uint32_t y = __shfl_xor(m, d, 64);
+    m = y > m ? y : m;
+  }
+  if ((threadIdx.x & 63) == 0) s_max[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = s_max[0];
+  for (int w = 1; w < 4; ++w) m = s_max[w] > m ? s_max[w] : m;
+  // p = floor(log2(max)) - 14 so that max * 2**-p lies in [2**14, 2**15)
+  int p = m ? (int)(m >> 23) - 127 - 14 : 0;
+  p = p < -110 ? -110 : p;
+  const float inv = __builtin_ldexpf(1.0f, -p);
+  uint16_t* orow = x16 + (size_t)t * H;
+  for (int i = threadIdx.x; i < H; i += 256) {
+    const _Float16 h = (_Float16)(bf16_to_f32(row[i]) * inv);
+    orow[i] = __builtin_bit_cast(uint16_t, h);
+  }
+  if (threadIdx.x == 0) scale[t] = __builtin_ldexpf(1.0f, p);
+}
+
+}  // namespace
+
+hipError_t launch_route(const int32_t* topk_ids, int A, int E, int tile_m, const RouteOut& o,
+                        hipStream_t s) {
+  const size_t lds = (size_t)(E + kRouteWaves * E) * sizeof(int);
+  hipLaunchKernelGGL(route_kernel, dim3(1), dim3(kRouteThreads), lds, s, topk_ids, A, E, tile_m,
+                     o);
+  return hipGetLastError();
+}
+
+hipError_t launch_rows_to_f16(const uint16_t* x, int T, int H, uint16_t* x16, float* scale,
+                              hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  hipLaunchKernelGGL(rows_to_f16_kernel, dim3(T), dim3(256), 0, s, x, T, H, x16, scale);
+  return hipGetLastError();
+}
+
+}  // namespace moefp4

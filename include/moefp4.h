@@ -1,0 +1,151 @@
+/*
+ * moefp4 -- block-scaled FP4 top-k mixture-of-experts forward and
+ * group16 -> group32 FP4 requantisation for AMD MI355X (gfx950).
+ *
+ * C ABI.  Every pointer argument named as device memory must point to memory
+ * allocated on the current HIP device; the library never allocates, frees or
+ * synchronises on these calls, and all work is enqueued on the caller's
+ * stream in order.  Host-side validation runs before any launch: a call that
+ * returns an error status has enqueued nothing, and moefp4_last_error()
+ * returns a message for it (thread-local, valid until the next call on the
+ * same thread).
+ *
+ * Sources (the pages this library implements; cited by title and section):
+ *  [P1] DeepGEMM commit log, branch "cch/deepgemm-glm52-nvfp4-group16":
+ *       requant_fp4_to_gran_k with separate source/destination scale packing
+ *       that recomputes UE8M0 scales; the explicit group16 capability gate of
+ *       the fused FP8xFP4 compute.
+ *  [P2] "GLM-5.2 NVFP4 group16 MegaMoE notes": sections Context (recipe
+ *       (1, 1, 32), group_size=16 checkpoints), Current patch scope,
+ *       Requantization path, Validation target.
+ *  [P3] b12x moe/fused/w4a16/prepare.py: raw [E, N, K/2] packed FP4 weights,
+ *       K/16 E4M3 block scales with a per-expert FP32 global scale
+ *       (prepare_w4a16_modelopt_nvfp4_weights), K/32 E8M0 scales
+ *       (prepare_w4a16_fp4_e8m0_k32_weights, _validate_e8m0_k32_scales),
+ *       gate/up order of the fused W13 rows (_normalize_w13_layout), per-call
+ *       buffers sized by tokens and top-k (make_w4a16_packed_buffers).
+ *
+ * Data layouts (row-major, K contiguous):
+ *  FP4 tensor  [E, N, K/2] uint8, two E2M1 codes per byte, element 2j in the
+ *              low nibble of byte j ([P3] _repack_4bit_no_perm reads a row as
+ *              little-endian int32 words, element pos at shift 4*pos).
+ *  scales      [E, N, K/gran] uint8: E4M3 (fn) for gran 16, UE8M0 for gran 32.
+ *  global      [E] float32 multiplier per expert per tensor, or NULL.
+ *              (compressed-tensors checkpoints store 1/gs: pass its inverse.)
+ */
+#ifndef MOEFP4_H
+#define MOEFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moefp4_status {
+  MOEFP4_OK = 0,
+  MOEFP4_EINVAL = 1,        /* bad shape, pointer or argument */
+  MOEFP4_EUNSUPPORTED = 2,  /* valid request this library does not compute */
+  MOEFP4_EWORKSPACE = 3,    /* workspace missing or too small */
+  MOEFP4_EHIP = 4           /* a HIP launch reported an error */
+} moefp4_status;
+
+/* Activation formats.
+ * BF16: x [T, H] bfloat16.
+ * FP8_UE8M0_K32: x [T, H] E4M3 (fn) bytes and x_sf [T, H/32] UE8M0 bytes,
+ *   value = fp8 * 2**(sf - 127) -- the activation side of the FP8xFP4
+ *   recipe (1, 1, 32) of [P2] Context. */
+typedef enum moefp4_act_fmt { MOEFP4_ACT_BF16 = 0, MOEFP4_ACT_FP8_UE8M0_K32 = 1 } moefp4_act_fmt;
+
+/* Order of the 2I rows of w13.  GATE_UP: rows [0, I) are the gate projection
+ * (the kernel-native "w31"/"gate_up" of [P3] _normalize_w13_layout).
+ * UP_GATE: rows [0, I) are the up projection ("w13"/"up_gate" checkpoint
+ * order, which [P3] _prepare_w4a16_packed_weights handles as a row rotation
+ * by I). */
+typedef enum moefp4_w13_order { MOEFP4_GATE_UP = 0, MOEFP4_UP_GATE = 1 } moefp4_w13_order;
+
+/* Output formats.  BF16: out [T, H] bfloat16, the FP32 result rounded to
+ * nearest even.  F32: out [T, H] float32, the FP32-accumulated result itself
+ * (the same value the BF16 output is rounded from). */
+typedef enum moefp4_out_fmt { MOEFP4_OUT_BF16 = 0, MOEFP4_OUT_F32 = 1 } moefp4_out_fmt;
+
+/* Problem description.  T tokens, E experts, top_k experts per token,
+ * H hidden size, I intermediate size (w13 has 2I rows), gran_k 16 or 32,
+ * act_fmt (moefp4_act_fmt), w13_order (moefp4_w13_order), out_fmt
+ * (moefp4_out_fmt). */
+typedef struct moefp4_problem {
+  int32_t T, E, top_k, H, I, gran_k, act_fmt, w13_order, out_fmt;
+} moefp4_problem;
+
+/* Workspace size for moe_fp4_route / moe_fp4_forward on problem p.
+ * Returns OK and writes *bytes, or EINVAL/EUNSUPPORTED for an invalid or
+ * unsupported problem.  The workspace is caller-owned device memory (the
+ * analogue of [P3] make_w4a16_packed_buffers and _make_workspace); its
+ * first 4 bytes hold, after a call completes, the number of assignments
+ * whose expert id was outside [0, E) and was therefore dropped. */
+moefp4_status moe_fp4_workspace_bytes(const moefp4_problem* p, size_t* bytes);
+
+/* Routing: groups the T*k assignments a = t*k + j by expert id, stably (ties
+ * in a-order).  Device outputs: counts [E], offsets [E+1] (exclusive prefix,
+ * offsets[E] = number of valid assignments), sorted_assign [T*k] (assignment
+ * ids in expert order, -1 past offsets[E]), slot_of [T*k] (inverse: position
+ * of assignment a in sorted_assign, -1 if dropped).  Ids outside [0, E) are
+ * dropped and counted in the workspace's first word.
+ * [P3] make_w4a16_packed_buffers sizes per-call buffers by tokens and top-k;
+ * the grouping itself is the "top-k routed tokens gathered per expert" step
+ * of the fused MoE. */
+moefp4_status moe_fp4_route(const moefp4_problem* p, const int32_t* topk_ids,
+                            int32_t* counts, int32_t* offsets,
+                            int32_t* sorted_assign, int32_t* slot_of,
+                            void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* MoE forward: out[t] = sum_j topk_w[t, j] * FC2_e(SwiGLU(FC1_e(x[t]))),
+ * e = topk_ids[t, j]; FC1 uses w13 [E, 2I, H/2] + w13_sf [E, 2I, H/gran]
+ * (+ w13_gs [E]), FC2 uses w2 [E, H, I/2] + w2_sf [E, H, I/gran] (+ w2_gs),
+ * SwiGLU h = silu(gate) * up; h is rounded to bfloat16 (BF16 activations) or
+ * quantised per 32 elements to E4M3 + UE8M0 (FP8 activations) before FC2;
+ * FP32 accumulation; out [T, H] bfloat16 or float32 (p->out_fmt).
+ * Supported: (BF16, gran 16), (BF16, gran 32), (FP8_UE8M0_K32, gran 32).
+ * FP8 activations with group16 weights return EUNSUPPORTED, like the
+ * capability gate on recipe (1, 1, 16) in [P1] / [P2] Current patch scope.
+ * x_sf must be NULL for BF16 and non-NULL for FP8.  All pointers device
+ * memory; topk_ids [T, k] int32, topk_w [T, k] float32. */
+moefp4_status moe_fp4_forward(const moefp4_problem* p,
+                              const void* x, const uint8_t* x_sf,
+                              const int32_t* topk_ids, const float* topk_w,
+                              const uint8_t* w13, const uint8_t* w13_sf, const float* w13_gs,
+                              const uint8_t* w2, const uint8_t* w2_sf, const float* w2_gs,
+                              void* out, void* workspace, size_t ws_bytes,
+                              hipStream_t stream);
+
+/* Requantise E x [N, K] FP4 from src_gran to dst_gran ([P2] Requantization
+ * path; [P1] requant_fp4_to_gran_k): dequantise with the group16 E4M3 scales
+ * and the optional per-expert global scale (src_gs [E] or NULL), then per
+ * block of 32 K elements choose UE8M0 e = ceil(log2(amax / 6)) (the smallest
+ * e with 6 * 2**e >= amax; byte 0 for an all-zero block) and round each value
+ * / 2**e to the nearest E2M1 code, ties to the even code, sign kept.  The
+ * global scale is folded into the result.  Bit-exact with the FP64
+ * definition whenever |gs| * 2688 and the smallest nonzero |gs| * 2**-10 are
+ * normal FP32 numbers.
+ * src [E, N, K/2], src_sf [E, N, K/16], dst [E, N, K/2], dst_sf [E, N, K/32],
+ * all device memory.  dst may equal src (in place); any other overlap among
+ * the four buffers is EINVAL.  Only src_gran 16 -> dst_gran 32 is computed
+ * (EUNSUPPORTED otherwise); K must be a multiple of 32. */
+moefp4_status fp4_requant_gran_k(int64_t E, int64_t N, int64_t K,
+                                 const uint8_t* src, const uint8_t* src_sf,
+                                 int32_t src_gran, const float* src_gs,
+                                 uint8_t* dst, uint8_t* dst_sf, int32_t dst_gran,
+                                 hipStream_t stream);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* moefp4_last_error(void);
+
+/* Library version string. */
+const char* moefp4_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOEFP4_H */

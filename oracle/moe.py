@@ -91,6 +91,57 @@ def quantize_h_a8(h):
     return hhat.reshape(n, I), q.reshape(n, I), (e + 127).astype(np.uint8)
 
 
+# A rounding decision of h is taken as undecided between its two
+# neighbouring results when h lies within DECISION_RADIUS * (max |h| of its
+# 32-element block) of the decision boundary.  An FP32-accumulated h (the
+# kernels') stays within about 2**-20 of that block maximum of the exact one,
+# cancellation included, so this leaves a wide margin.
+DECISION_RADIUS = 2.0 ** -14
+
+
+def _grid_ambiguity(y, mant_bits, emin, radius):
+    """|alternative rounding - RNE rounding| of each exact value y when y lies
+    within ``radius`` (absolute, same units as y) of a rounding midpoint of the
+    float grid with ``mant_bits`` fraction bits and minimum normal exponent
+    ``emin``; 0 elsewhere."""
+    y = np.abs(np.asarray(y, dtype=np.float64))
+    _, ex = np.frexp(y)
+    e = np.maximum(ex.astype(np.int64) - 1, emin)
+    quantum = np.ldexp(1.0, e - mant_bits)
+    frac = y / quantum - np.floor(y / quantum)
+    near = np.abs(frac - 0.5) * quantum <= radius
+    return np.where(near, quantum, 0.0)
+
+
+def h_decision_band(h, a8, radius=DECISION_RADIUS):
+    """Per element, the largest change of the quantised h that a rounding
+    decision within ``radius`` * (block max |h|) could make: one grid step
+    where h is that close to a rounding midpoint and, for A8, the whole
+    requantisation of a 32-block under the neighbouring exponent where amax
+    is that close to 448 * 2**e.  Zero where every decision is clear."""
+    h = np.asarray(h, dtype=np.float64)
+    n, I = h.shape
+    blk = h.reshape(n, I // 32, 32)
+    amax = np.max(np.abs(blk), axis=-1)
+    rad = radius * amax[..., None]
+    if not a8:
+        return _grid_ambiguity(blk, 7, -126, rad).reshape(n, I)
+    hhat, _, sb = quantize_h_a8(h)
+    hhat = hhat.reshape(n, I // 32, 32)
+    e = sb.astype(np.int64) - 127
+    band = _grid_ambiguity(np.ldexp(blk, -e[..., None]), 3, -6,
+                           np.ldexp(rad, -e[..., None])) * np.ldexp(1.0, e[..., None])
+    for de in (-1, 1):
+        e2 = e + de
+        lim = np.ldexp(448.0, np.minimum(e, e2))  # the boundary between e and e2
+        close = (amax > 0) & (np.abs(amax - lim) <= radius * amax)
+        if np.any(close):
+            alt = np.ldexp(e4m3_decode(rne_e4m3(np.clip(np.ldexp(blk, -e2[..., None]), -448, 448))),
+                           e2[..., None])
+            band = np.where(close[..., None], np.maximum(band, np.abs(alt - hhat)), band)
+    return band.reshape(n, I)
+
+
 def decode_activations(x, x_sf=None):
     """A16: x is [T, H] bfloat16 bit patterns (uint16).  A8: x is [T, H]
     E4M3 bytes and x_sf [T, H/32] UE8M0 bytes; value = fp8 * 2**(sf - 127)."""
@@ -102,7 +153,7 @@ def decode_activations(x, x_sf=None):
 
 def moe_forward(x, topk_ids, topk_w, w13, w13_sf, w13_gs, w2, w2_sf, w2_gs,
                 gran: int, x_sf=None, w13_order: str = "gate_up",
-                tokens=None, out_cols=None, return_parts=False):
+                tokens=None, out_cols=None, return_parts=False, return_band=False):
     """FP64 MoE forward.  Shapes: x [T, H] (see decode_activations),
     topk_ids/topk_w [T, k], w13 [E, 2I, H/2], w13_sf [E, 2I, H/gran],
     w2 [E, H, I/2], w2_sf [E, H, I/gran], gs [E] float32 or None.
@@ -114,6 +165,11 @@ def moe_forward(x, topk_ids, topk_w, w13, w13_sf, w13_gs, w2, w2_sf, w2_gs,
     ``tokens`` / ``out_cols`` restrict the computation to a subset of output
     rows / columns (each output element is computed by the same definition);
     the result is then [len(tokens), len(out_cols)].
+
+    ``return_band``: also return, per output element, the largest change
+    that near-tie rounding decisions of h (see h_decision_band) can cause:
+    sum_j |w| * sum_i band_i * |W2[n, i]|.  Every result inside
+    out +- band is an equally valid outcome of the quantisation rule.
     """
     ids = np.asarray(topk_ids, dtype=np.int64)
     w = np.asarray(topk_w, dtype=np.float32).astype(np.float64)
@@ -133,6 +189,7 @@ def moe_forward(x, topk_ids, topk_w, w13, w13_sf, w13_gs, w2, w2_sf, w2_gs,
         want[t * k:(t + 1) * k] = True
 
     Y = {}  # slot -> FP64 row over out_cols
+    YB = {}  # slot -> decision band row
     for e in range(E):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
         assigns = [int(a) for a in sorted_assign[lo:hi] if want[a]]
@@ -155,15 +212,25 @@ def moe_forward(x, topk_ids, topk_w, w13, w13_sf, w13_gs, w2, w2_sf, w2_gs,
         W2 = dequant_fp4(np.asarray(w2[e])[out_cols], np.asarray(w2_sf[e])[out_cols],
                          gran, kind, gs2)
         Ye = hhat @ W2.T
+        if return_band:
+            YBe = h_decision_band(h, a8) @ np.abs(W2).T
         for r, a in enumerate(assigns):
             Y[int(slot_of[a])] = Ye[r]
+            if return_band:
+                YB[int(slot_of[a])] = YBe[r]
 
     out = np.zeros((len(tokens), len(out_cols)), dtype=np.float64)
+    band = np.zeros_like(out)
     for r, t in enumerate(tokens):
         for j in range(k):
             s = int(slot_of[t * k + j])
             if s >= 0:
                 out[r] += w[t, j] * Y[s]
+                if return_band:
+                    band[r] += abs(w[t, j]) * YB[s]
+    res = (out,)
     if return_parts:
-        return out, (counts, offsets, sorted_assign, slot_of)
-    return out
+        res += ((counts, offsets, sorted_assign, slot_of),)
+    if return_band:
+        res += (band,)
+    return res[0] if len(res) == 1 else res

@@ -30,7 +30,7 @@ import torch
 
 # stream ids
 _S_ROUTER, _S_X = 1, 2
-_S_W13, _S_W13SF, _S_W2, _S_W2SF, _S_GS = 10, 11, 12, 13, 14
+_S_W13, _S_W2, _S_GS = 10, 12, 14
 
 
 def _rng(*key) -> np.random.Generator:
@@ -53,6 +53,11 @@ class MoEConfig:
     global_scale: str = "uniform"       # "uniform" U[0.5, 2], "one", "none"
     zipf_s: float = 1.1
     seed: int = 0
+    weight_seed: int | None = None      # weights drawn from this seed (default: seed)
+
+    @property
+    def wseed(self) -> int:
+        return self.seed if self.weight_seed is None else self.weight_seed
 
 
 @dataclass(frozen=True)
@@ -73,12 +78,15 @@ CONFIGS = {
     "decode32": MoEConfig("decode32", T=256, E=256, k=8, H=6144, I=2048, gran=32,
                           act="fp8", routing="softmax_topk", global_scale="none",
                           seed=2),
+    # the prefill layer reuses the decode32 layer's weights (same weight seed)
     "prefill32": MoEConfig("prefill32", T=8192, E=256, k=8, H=6144, I=2048, gran=32,
-                           act="fp8", routing="zipf", global_scale="none", seed=3),
+                           act="fp8", routing="zipf", global_scale="none", seed=3,
+                           weight_seed=2),
 }
 
 REQUANT_CONFIGS = {
-    "requant": RequantConfig("requant", E=256, shapes=((4096, 6144), (6144, 2048)), seed=4),
+    # the full decode16 layer (same seed and streams): w13 and w2 of 256 experts
+    "requant": RequantConfig("requant", E=256, shapes=((4096, 6144), (6144, 2048)), seed=1),
 }
 
 
@@ -207,13 +215,14 @@ def make_moe_inputs(cfg: MoEConfig) -> MoEInputs:
     w13_sf = np.empty((E, 2 * I, H // g), np.uint8)
     w2 = np.empty((E, H, I // 2), np.uint8)
     w2_sf = np.empty((E, H, I // g), np.uint8)
+    ws = cfg.wseed
     for e in range(E):
-        w13[e], w13_sf[e] = make_fp4_tensor(cfg.seed, _S_W13, e, 2 * I, H, g,
+        w13[e], w13_sf[e] = make_fp4_tensor(ws, _S_W13, e, 2 * I, H, g,
                                             cfg.scale_log2, cfg.ue8m0_exp)
-        w2[e], w2_sf[e] = make_fp4_tensor(cfg.seed, _S_W2, e, H, I, g,
+        w2[e], w2_sf[e] = make_fp4_tensor(ws, _S_W2, e, H, I, g,
                                           cfg.scale_log2, cfg.ue8m0_exp)
-    gs1 = make_global_scales(cfg.seed, _S_W13, E, cfg.global_scale)
-    gs2 = make_global_scales(cfg.seed, _S_W2, E, cfg.global_scale)
+    gs1 = make_global_scales(ws, _S_W13, E, cfg.global_scale)
+    gs2 = make_global_scales(ws, _S_W2, E, cfg.global_scale)
     return MoEInputs(cfg, x, x_sf, ids, w, w13, w13_sf, gs1, w2, w2_sf, gs2)
 
 

@@ -1,0 +1,107 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+the header declares, and host-side validation returns the documented status
+codes (with a message) before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_scaled_fp4_topk_amd as m
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moefp4.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(\w+)\s*\([^;{]*\)\s*;", text)) - {"if", "while"})
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(m.LIB_PATH):
+        pytest.fail("libmoefp4.so is not built (python -m block_scaled_fp4_topk_amd.build)")
+    return m.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert {"moe_fp4_forward", "moe_fp4_route", "fp4_requant_gran_k", "moe_fp4_workspace_bytes",
+            "moefp4_last_error", "moefp4_version"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+    assert b"gfx950" in L.moefp4_version()
+
+
+def P(**kw):
+    d = dict(T=64, E=256, top_k=8, H=6144, I=2048, gran_k=16, act_fmt=0, w13_order=0, out_fmt=0)
+    d.update(kw)
+    return m.Problem(**d)
+
+
+def ws_status(p):
+    n = ctypes.c_size_t(0)
+    return m.lib().moe_fp4_workspace_bytes(ctypes.byref(p), ctypes.byref(n)), n.value
+
+
+def test_workspace_sizes(L):
+    st, n = ws_status(P())
+    assert st == 0 and n > 512 * 6144 * 4  # holds the f32 FC2 rows
+    st8, n8 = ws_status(P(T=8192, gran_k=32, act_fmt=1))
+    assert st8 == 0 and n8 > 65536 * 6144 * 4
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(gran_k=8), m.EINVAL),
+    (dict(top_k=0), m.EINVAL),
+    (dict(top_k=300), m.EINVAL),
+    (dict(E=0), m.EINVAL),
+    (dict(E=4096, top_k=8), m.EUNSUPPORTED),
+    (dict(H=6000), m.EINVAL),
+    (dict(I=2000), m.EINVAL),
+    (dict(I=2080), m.EUNSUPPORTED),
+    (dict(act_fmt=1, gran_k=16), m.EUNSUPPORTED),
+    (dict(act_fmt=7), m.EINVAL),
+    (dict(w13_order=3), m.EINVAL),
+    (dict(out_fmt=2), m.EINVAL),
+    (dict(T=-1), m.EINVAL),
+])
+def test_problem_validation(L, kw, status):
+    st, _ = ws_status(P(**kw))
+    assert st == status
+    assert len(L.moefp4_last_error()) > 0
+
+
+def test_forward_rejects_before_launch(L):
+    p = P()
+    z = ctypes.c_void_p(0)
+    # NULL tensors
+    st = L.moe_fp4_forward(ctypes.byref(p), z, z, z, z, z, z, z, z, z, z, z, z, 0, z)
+    assert st == m.EINVAL and b"non-NULL" in L.moefp4_last_error()
+    # fake (never dereferenced) aligned pointers, missing workspace
+    f = ctypes.c_void_p(1 << 20)
+    st = L.moe_fp4_forward(ctypes.byref(p), f, z, f, f, f, f, z, f, f, z, f, z, 0, z)
+    assert st == m.EWORKSPACE
+    # x_sf given for bf16 activations
+    st = L.moe_fp4_forward(ctypes.byref(p), f, f, f, f, f, f, z, f, f, z, f, f, 1 << 40, z)
+    assert st == m.EINVAL and b"x_sf" in L.moefp4_last_error()
+    # T = 0 is a valid empty call
+    p0 = P(T=0)
+    assert L.moe_fp4_forward(ctypes.byref(p0), z, z, z, z, z, z, z, z, z, z, z, z, 0, z) == 0
+
+
+def test_requant_rejects_before_launch(L):
+    z = ctypes.c_void_p(0)
+    f = ctypes.c_void_p(1 << 20)
+    g = ctypes.c_void_p(1 << 30)
+    rq = L.fp4_requant_gran_k
+    assert rq(2, 4, 64, f, g, 32, z, f, g, 16, z) == m.EUNSUPPORTED
+    assert rq(2, 4, 64, f, g, 16, z, f, g, 64, z) == m.EINVAL
+    assert rq(2, 4, 48, f, g, 16, z, f, g, 32, z) == m.EINVAL            # K % 32
+    assert rq(2, 4, 64, z, g, 16, z, f, g, 32, z) == m.EINVAL            # NULL src
+    assert rq(2, 4, 64, f, f, 16, z, ctypes.c_void_p(1 << 24), g, 32, z) == m.EINVAL  # src_sf overlaps src
+    assert rq(0, 4, 64, z, z, 16, z, z, z, 32, z) == 0                   # empty
+    assert rq(2, 4, 64, ctypes.c_void_p((1 << 20) + 8), g, 16, z, f, ctypes.c_void_p(1 << 31), 32, z) == m.EINVAL

@@ -1,0 +1,117 @@
+"""MoE forward on the GPU vs the FP64 oracle, within the stated bound
+(max |err| <= 2e-2 rms(ref), mean relative error <= 5e-3): every supported
+(activation, scale) combination, both w13 row orders, ragged tiles, the
+multi-tile prefill path, duplicate and out-of-range expert ids, bitwise
+determinism, and the full-size workloads on sampled tokens."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from helpers import check_bound, check_forward, gpu_forward, require_gpu, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def ref_forward(inp, order="gate_up", tokens=None, out_cols=None):
+    """(FP64 output, decision band) of the oracle."""
+    return oracle.moe_forward(inp.x, inp.topk_ids, inp.topk_w, inp.w13, inp.w13_sf, inp.w13_gs,
+                              inp.w2, inp.w2_sf, inp.w2_gs, inp.cfg.gran, x_sf=inp.x_sf,
+                              w13_order=order, tokens=tokens, out_cols=out_cols,
+                              return_band=True)
+
+
+def combos(base):
+    return [
+        synth.variant(base, gran=16, act="bf16", global_scale="uniform"),
+        synth.variant(base, gran=32, act="bf16", global_scale="none"),
+        synth.variant(base, gran=32, act="bf16", global_scale="uniform"),
+        synth.variant(base, gran=32, act="fp8", global_scale="none"),
+    ]
+
+
+def _id(c):
+    return f"{c.act}-g{c.gran}-{c.global_scale}-T{c.T}-E{c.E}-k{c.k}-H{c.H}-I{c.I}"
+
+
+SMALL = (combos(synth.CONFIGS["tiny"])
+         + combos(synth.variant(synth.CONFIGS["tiny"], T=16, E=32, k=4, H=1024, I=512, seed=21))
+         + combos(synth.variant(synth.CONFIGS["tiny"], T=13, E=6, k=3, H=768, I=256, seed=22))
+         + combos(synth.variant(synth.CONFIGS["tiny"], T=300, E=8, k=2, H=512, I=512, seed=23,
+                                routing="zipf")))
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=[_id(c) for c in SMALL])
+def test_forward_small(cfg):
+    require_gpu()
+    print("forward", _id(cfg), flush=True)
+    inp = synth.make_moe_inputs(cfg)
+    d = to_dev(inp)
+    for order in ("gate_up", "up_gate"):
+        ref, band = ref_forward(inp, order)
+        check_forward(inp, d, ref, f"{_id(cfg)} {order}", order, band)
+
+
+def test_duplicate_and_dropped_ids():
+    require_gpu()
+    cfg = synth.variant(synth.CONFIGS["tiny"], T=24, E=8, k=3, seed=31)
+    inp = synth.make_moe_inputs(cfg)
+    ids = inp.topk_ids.copy()
+    ids[0, 1] = ids[0, 0]          # same expert twice in one token
+    ids[1, 2] = -1                 # dropped
+    ids[2, 0] = 8                  # dropped
+    ids[3] = ids[3, 0]             # all three picks the same expert
+    inp.topk_ids = ids
+    d = to_dev(inp)
+    ref, band = ref_forward(inp)
+    check_forward(inp, d, ref, "dup+dropped", band=band)
+
+
+def test_deterministic():
+    require_gpu()
+    for base in (synth.variant(synth.CONFIGS["tiny"], T=64, E=32, k=8, H=1024, I=512, seed=41),
+                 synth.variant(synth.CONFIGS["tiny"], T=512, E=8, k=2, H=512, I=512, seed=42,
+                               routing="zipf", gran=32, act="fp8", global_scale="none")):
+        inp = synth.make_moe_inputs(base)
+        d = to_dev(inp)
+        a = gpu_forward(inp, d, out_dtype=torch.float32).clone()
+        b = gpu_forward(inp, d, out_dtype=torch.float32).clone()
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+_FULL = {}
+
+
+def full_inputs(name):
+    if name not in _FULL:
+        print(f"generating full {name} inputs", flush=True)
+        inp = synth.make_moe_inputs(synth.CONFIGS[name])
+        _FULL.clear()
+        _FULL[name] = (inp, to_dev(inp))
+    return _FULL[name]
+
+
+@pytest.mark.parametrize("name", ["decode16", "decode32", "prefill32"])
+def test_full_size_sampled(name):
+    """The full workload in the launch configuration the benchmark times;
+    the oracle computes a sample of tokens (including one routed to the most
+    loaded expert) over a sample of output columns."""
+    require_gpu()
+    inp, d = full_inputs(name)
+    print(f"{name}: running on GPU", flush=True)
+    out = gpu_forward(inp, d, out_dtype=torch.float32)
+    b16 = gpu_forward(inp, d)
+    torch.cuda.synchronize()
+    assert torch.equal(out.to(torch.bfloat16).view(torch.int16), b16.view(torch.int16))
+    rng = np.random.default_rng(0)
+    counts = np.bincount(inp.topk_ids.ravel(), minlength=inp.cfg.E)
+    heavy = int(np.flatnonzero((inp.topk_ids == counts.argmax()).any(axis=1))[0])
+    tokens = sorted({0, inp.cfg.T - 1, heavy, int(rng.integers(inp.cfg.T))})
+    cols = np.sort(rng.choice(inp.cfg.H, size=768, replace=False))
+    print(f"{name}: oracle on tokens {tokens}", flush=True)
+    ref, band = ref_forward(inp, tokens=tokens, out_cols=cols)
+    got = out[tokens][:, torch.from_numpy(cols).cuda()].cpu().numpy().astype(np.float64)
+    check_bound(got, ref, f"{name} sampled", band)

@@ -250,3 +250,31 @@ def test_a8_forward_brute_force():
             for n in range(64):
                 ref[t, n] += float(inp.topk_w[t, j]) * sum(hq[i] * W2[n, i] for i in range(64))
     assert np.allclose(got, ref, rtol=1e-9, atol=1e-9 * np.abs(ref).max())
+
+
+def test_decision_band():
+    """The band is one grid step exactly for values within the radius (times
+    the block maximum) of a rounding midpoint, zero elsewhere, and covers the
+    neighbouring exponent when a block maximum sits on 448 * 2**e."""
+    # bf16, block max 4: radius 4 * 2**-14 = 2**-12.  1 + 2**-8 is a midpoint
+    # (step 2**-7); 1 + 2**-8 + 2**-13 is within the radius, + 2**-11 is not
+    h = np.zeros((1, 32))
+    h[0, :5] = [1.0 + 2.0 ** -8, 1.0 + 2.0 ** -8 + 2.0 ** -13, 1.0 + 2.0 ** -8 + 2.0 ** -11,
+                1.0 + 2.0 ** -9, 4.0]
+    b = oracle.h_decision_band(h, a8=False)
+    assert list(b[0, :5]) == [2.0 ** -7, 2.0 ** -7, 0.0, 0.0, 0.0] and not b[0, 5:].any()
+    # E4M3, block max 300 (e = 0, radius 300 * 2**-14 ~ 0.018): the midpoint
+    # 1 + 2**-4 is ambiguous by one step (0.125); 2.3 is clear; a value in the
+    # subnormal range is ambiguous by its quantum 2**-9 (its half-step is
+    # smaller than the radius)
+    blk = np.zeros((1, 32))
+    blk[0, :4] = [300.0, 1.0 + 2.0 ** -4, 2.3, 3 * 2.0 ** -9]
+    b = oracle.h_decision_band(blk, a8=True)
+    assert b[0, 0] == 0 and b[0, 1] == 0.125 and b[0, 2] == 0 and b[0, 3] == 2.0 ** -9
+    # block max on the exponent boundary 448 * 2**0: the band covers the
+    # requantisation of the whole block with e = 1
+    blk[0, 0] = 448.0
+    b = oracle.h_decision_band(blk, a8=True)
+    prim = oracle.quantize_h_a8(blk)[0]
+    alt = np.ldexp(oracle.e4m3_decode(oracle.rne_e4m3(blk / 2.0)), 1)
+    assert np.all(b >= np.abs(alt - prim)) and np.any(alt != prim)
