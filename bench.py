@@ -1,0 +1,316 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-scaled FP4 top-k MoE forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode16]
+
+One step = one moe_fp4_forward call (routing, FC1 + SwiGLU, FC2, router-
+weighted combine) over one batch of synthetic input already resident in HBM.
+The default workload is the W4A16 NVFP4 group16 decode layer (T=64 tokens,
+E=256 experts, top-8, H=6144, I=2048).  Prints ONE JSON line with tokens/s,
+the HBM roofline of the dominant kernel (HIP events recorded by the library
+on the launch stream around each stage), the whole-forward roofline, the
+FP64 oracle timed on the host cores on a bounded sample (cpu_baseline), and
+secondary figures for the other workloads of the hot path (FP8xFP4 decode,
+prefill, group16 -> group32 requantisation of the whole layer).
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "FP4 MoE fwd tokens/s + achieved HBM GB/s (decode) / MFMA TFLOP/s (prefill) vs peak"
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "fp8": 5000.0, "fp4": 10100.0}
+WORKLOAD_TEXT = {
+    "decode16": "W4A16 NVFP4 decode: T=64 E=256 top-8 H=6144 I=2048, bf16 x, E2M1 + E4M3 k16 + fp32 global",
+    "decode32": "FP8xFP4 decode: T=256 E=256 top-8 H=6144 I=2048, E4M3+UE8M0 k32 x, E2M1 + UE8M0 k32",
+    "prefill32": "prefill: T=8192 E=256 top-8 Zipf(1.1) H=6144 I=2048, E4M3+UE8M0 k32 x, E2M1 + UE8M0 k32",
+}
+DTYPE = {"decode16": "f16", "decode32": "fp8xfp4", "prefill32": "fp8xfp4"}
+STAGES = ["route", "act_prep", "fc1_swiglu", "fc2", "combine"]
+
+
+class HipEvents:
+    """Raw hipEvent_t handles (the library records them on its launch stream)."""
+
+    def __init__(self, n):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            if self.hip.hipEventCreate(ctypes.byref(self.arr, i * ctypes.sizeof(ctypes.c_void_p))) != 0:
+                raise RuntimeError("hipEventCreate failed")
+
+    def sub(self, i0, n):
+        return ctypes.cast(ctypes.byref(self.arr, i0 * ctypes.sizeof(ctypes.c_void_p)),
+                           ctypes.POINTER(ctypes.c_void_p))
+
+    def ms(self, i, j):
+        f = ctypes.c_float(0)
+        if self.hip.hipEventElapsedTime(ctypes.byref(f), ctypes.c_void_p(self.arr[i]),
+                                        ctypes.c_void_p(self.arr[j])) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return f.value
+
+
+def to_dev(torch, inp):
+    d = {}
+    if inp.x_sf is None:
+        d["x"] = torch.from_numpy(inp.x.view(np.int16)).view(torch.bfloat16).cuda()
+        d["x_sf"] = None
+    else:
+        d["x"] = torch.from_numpy(inp.x).cuda()
+        d["x_sf"] = torch.from_numpy(inp.x_sf).cuda()
+    d["topk_ids"] = torch.from_numpy(inp.topk_ids).cuda()
+    d["topk_w"] = torch.from_numpy(inp.topk_w).cuda()
+    for n in ("w13", "w13_sf", "w2", "w2_sf"):
+        d[n] = torch.from_numpy(getattr(inp, n)).cuda()
+    for n in ("w13_gs", "w2_gs"):
+        v = getattr(inp, n)
+        d[n] = None if v is None else torch.from_numpy(v).cuda()
+    return d
+
+
+def gpu_forward_into(moe, torch, inp, d, ws, out):
+    """One forward; allocates the workspace and output on the first call."""
+    if ws is None:
+        c = inp.cfg
+        p = moe.make_problem(c.T, c.E, c.k, c.H, c.I, c.gran,
+                             moe.ACT_FP8_UE8M0_K32 if c.act == "fp8" else moe.ACT_BF16)
+        ws = torch.empty(moe.workspace_bytes(p), dtype=torch.uint8, device="cuda")
+        out = torch.empty((c.T, c.H), dtype=torch.bfloat16, device="cuda")
+    moe.forward(d["x"], d["topk_ids"], d["topk_w"], d["w13"], d["w13_sf"], d["w13_gs"], d["w2"],
+                d["w2_sf"], d["w2_gs"], inp.cfg.gran, x_sf=d["x_sf"], out=out, workspace=ws)
+    return ws, out
+
+
+def algorithmic_bytes(cfg, ids):
+    """Compulsory HBM bytes: the weights (codes, block scales, global scales)
+    of every expert that receives at least one token, the activations read
+    once, the output written once, ids and router weights; and the FC1 /
+    FC2 kernel shares (FC1: w13 + x + h written; FC2: w2 + h read + rows of
+    f32 partial outputs written)."""
+    E, H, I, T, k, g = cfg.E, cfg.H, cfg.I, cfg.T, cfg.k, cfg.gran
+    active = int(np.unique(ids[(ids >= 0) & (ids < E)]).size)
+    A = T * k
+    gs = 0 if cfg.global_scale == "none" else 4
+    w13 = 2 * I * H // 2 + 2 * I * H // g + gs
+    w2 = H * I // 2 + H * I // g + gs
+    if cfg.act == "bf16":
+        x_bytes, h_bytes = T * H * 2, A * I * 2
+    else:
+        x_bytes, h_bytes = T * H + T * H // 32, A * I + A * I // 32
+    whole = active * (w13 + w2) + x_bytes + T * H * 2 + T * k * 8
+    fc1 = active * w13 + x_bytes + h_bytes
+    fc2 = active * w2 + h_bytes + A * H * 4
+    return dict(active=active, whole=whole, fc1=fc1, fc2=fc2)
+
+
+def flops(cfg):
+    return 2.0 * cfg.T * cfg.k * 3 * cfg.I * cfg.H
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(os.path.join(ROOT, "block_scaled_fp4_topk_amd", "csrc"))):
+        with open(os.path.join(ROOT, "block_scaled_fp4_topk_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def pmc_traffic(kernel_key, workload):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
+    --pmc summary, if it was taken on the current kernel sources; else None."""
+    p = os.path.join(ROOT, "profiles", f"{kernel_key}_{workload}_pmc.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        d = json.load(f)
+    if d.get("source_hash") != kernel_source_hash():
+        return None
+    return d.get("traffic_bytes_per_launch")
+
+
+def run_forward_timed(moe, torch, inp, d, steps, warmup):
+    """Warm up, then time `steps` forwards (synchronised on both sides) with
+    per-stage HIP events recorded by the library on the launch stream."""
+    ws, out = gpu_forward_into(moe, torch, inp, d, None, None)
+    for _ in range(warmup):
+        gpu_forward_into(moe, torch, inp, d, ws, out)
+    torch.cuda.synchronize()
+    ev = HipEvents(6 * steps)
+    t0 = time.perf_counter()
+    for i in range(steps):
+        moe.set_stage_events(ev.sub(6 * i, 6), 6)
+        gpu_forward_into(moe, torch, inp, d, ws, out)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    moe.set_stage_events(None, 0)
+    stage_ms = {name: float(np.mean([ev.ms(6 * i + s, 6 * i + s + 1) for i in range(steps)]))
+                for s, name in enumerate(STAGES)}
+    fwd_ms = float(np.mean([ev.ms(6 * i, 6 * i + 5) for i in range(steps)]))
+    return (t1 - t0) * 1e3 / steps, fwd_ms, stage_ms
+
+
+def cpu_baseline(inp, budget_s=15.0):
+    """The FP64 oracle as it stands, on this host, on a bounded sample of the
+    same workload: whole tokens (all their experts, all H outputs) until about
+    budget_s seconds of work; tokens/s = tokens done / time."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # noqa: BLE001
+        blas = 1
+    done, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < budget_s and done < inp.cfg.T:
+        oracle.moe_forward(inp.x, inp.topk_ids, inp.topk_w, inp.w13, inp.w13_sf, inp.w13_gs,
+                           inp.w2, inp.w2_sf, inp.w2_gs, inp.cfg.gran, x_sf=inp.x_sf,
+                           tokens=[done])
+        done += 1
+    dt = time.perf_counter() - t0
+    return {"value": done / dt, "unit": "tokens/s", "cores": blas, "kind": "oracle",
+            "sample": f"{done} whole token(s) of the {inp.cfg.name} workload (all {inp.cfg.k} experts, "
+                      f"all {inp.cfg.H} outputs), {dt:.1f} s; numpy FP64, BLAS threads={blas}, "
+                      f"elementwise work single-threaded"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode16", choices=list(WORKLOAD_TEXT))
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile", action="store_true",
+                    help="only the primary workload (for rocprofv3 runs)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_scaled_fp4_topk_amd as moe
+    import synth
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    moe.lib()  # fails loudly if the HIP library is not built
+
+    cfg = synth.CONFIGS[args.workload]
+    print(f"[bench] generating {cfg.name} inputs", file=sys.stderr, flush=True)
+    inp = synth.make_moe_inputs(cfg)
+    d = to_dev(torch, inp)
+    print("[bench] timing", file=sys.stderr, flush=True)
+    ms_step, fwd_ms, stage_ms = run_forward_timed(moe, torch, inp, d, args.steps, args.warmup)
+    ab = algorithmic_bytes(cfg, inp.topk_ids)
+    dom = max(("fc1_swiglu", "fc2"), key=lambda s: stage_ms[s])
+    dom_bytes = ab["fc1"] if dom == "fc1_swiglu" else ab["fc2"]
+    achieved = dom_bytes / (stage_ms[dom] * 1e-3) / 1e9
+    kernel_key = {"fc1_swiglu": "fc1", "fc2": "fc2"}[dom] + ("_a8" if cfg.act == "fp8" else "_a16")
+    res = {
+        "metric": METRIC,
+        "value": cfg.T / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": DTYPE[cfg.name],
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_TEXT[cfg.name], "T": cfg.T, "E": cfg.E, "top_k": cfg.k,
+                   "H": cfg.H, "I": cfg.I, "gran_k": cfg.gran, "act": cfg.act,
+                   "active_experts": ab["active"], "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": kernel_key, "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": pmc_traffic(kernel_key, cfg.name),
+                     "algorithmic_bytes_per_launch": dom_bytes, "launch_ms": stage_ms[dom]},
+        "forward": {"event_ms": fwd_ms, "stage_ms": stage_ms, "algorithmic_bytes": ab["whole"],
+                    "achieved_GBps": ab["whole"] / (fwd_ms * 1e-3) / 1e9,
+                    "hbm_frac": ab["whole"] / (fwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                    "tflops": flops(cfg) / (fwd_ms * 1e-3) / 1e12},
+    }
+    if not args.no_cpu_baseline and not args.profile:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(inp)
+    if not args.no_secondary and not args.profile:
+        res["secondary"] = secondary(moe, torch, synth, args, inp, d)
+    print(json.dumps(res), flush=True)
+
+
+def secondary(moe, torch, synth, args, inp16, d16):
+    """The other workloads of the hot path, each timed the same way."""
+    out = {}
+    del d16
+    torch.cuda.empty_cache()
+    # group16 -> group32 requantisation of the whole decode16 layer (its weights)
+    src13 = torch.from_numpy(inp16.w13).cuda()
+    sf13 = torch.from_numpy(inp16.w13_sf).cuda()
+    gs13 = torch.from_numpy(inp16.w13_gs).cuda()
+    src2 = torch.from_numpy(inp16.w2).cuda()
+    sf2 = torch.from_numpy(inp16.w2_sf).cuda()
+    gs2 = torch.from_numpy(inp16.w2_gs).cuda()
+    d13, s13 = torch.empty_like(src13), torch.empty(src13.shape[:2] + (src13.shape[2] * 2 // 32,),
+                                                    dtype=torch.uint8, device="cuda")
+    d2, s2 = torch.empty_like(src2), torch.empty(src2.shape[:2] + (src2.shape[2] * 2 // 32,),
+                                                 dtype=torch.uint8, device="cuda")
+
+    def rq():
+        moe.requant_gran_k(src13, sf13, gs13, dst=d13, dst_sf=s13)
+        moe.requant_gran_k(src2, sf2, gs2, dst=d2, dst_sf=s2)
+
+    for _ in range(2):
+        rq()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 5
+    e0.record()
+    for _ in range(n):
+        rq()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    nbytes = sum(int(t.numel()) for t in (src13, sf13, d13, s13, src2, sf2, d2, s2)) + 2 * 256 * 4
+    out["requant_layer"] = {"workload": "requant w13 [256,4096,6144] + w2 [256,6144,2048] g16 -> g32",
+                            "ms": ms, "algorithmic_bytes": nbytes,
+                            "achieved_GBps": nbytes / (ms * 1e-3) / 1e9,
+                            "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    del src13, sf13, gs13, src2, sf2, gs2, d13, s13, d2, s2
+    torch.cuda.empty_cache()
+    for name in ("decode32", "prefill32"):
+        cfg = synth.CONFIGS[name]
+        print(f"[bench] secondary {name}", file=sys.stderr, flush=True)
+        inp = synth.make_moe_inputs(cfg)
+        d = to_dev(torch, inp)
+        steps = 10 if name == "prefill32" else 20
+        ms_step, fwd_ms, stage_ms = run_forward_timed(moe, torch, inp, d, steps, 3)
+        ab = algorithmic_bytes(cfg, inp.topk_ids)
+        r = {"workload": WORKLOAD_TEXT[name], "ms_per_step": ms_step, "tokens_per_s": cfg.T / (ms_step * 1e-3),
+             "stage_ms": stage_ms, "algorithmic_bytes": ab["whole"],
+             "hbm_frac": ab["whole"] / (fwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+             "tflops": flops(cfg) / (fwd_ms * 1e-3) / 1e12}
+        r["mfma_frac_fp8_peak"] = r["tflops"] / PEAK_TFLOPS["fp8"]
+        out[name] = r
+        del d
+        torch.cuda.empty_cache()
+    return out
+
+
+if __name__ == "__main__":
+    main()

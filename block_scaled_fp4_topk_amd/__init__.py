@@ -66,6 +66,8 @@ def lib():
         L.fp4_requant_gran_k.restype = st
         L.moefp4_last_error.argtypes = []
         L.moefp4_last_error.restype = ctypes.c_char_p
+        L.moefp4_set_stage_events.argtypes = [_P, ctypes.c_int32]
+        L.moefp4_set_stage_events.restype = st
         L.moefp4_version.argtypes = []
         L.moefp4_version.restype = ctypes.c_char_p
         _lib = L
@@ -193,6 +195,12 @@ def requant_gran_k(src, src_sf, src_gs=None, src_gran=16, dst_gran=32, dst=None,
     _check(lib().fp4_requant_gran_k(E, N, K, _ptr(src), _ptr(src_sf), src_gran, _ptr(src_gs),
                                     _ptr(dst), _ptr(dst_sf), dst_gran, _stream(stream)))
     return dst, dst_sf
+
+
+def set_stage_events(events_array, n: int):
+    """Profiling hook (moefp4_set_stage_events): events_array is a ctypes
+    array of 6 hipEvent_t handles, or None to stop recording."""
+    _check(lib().moefp4_set_stage_events(events_array, n))
 
 
 def dropped_assignments(workspace) -> int:

@@ -15,6 +15,11 @@
 namespace {
 
 thread_local std::string g_err;
+thread_local hipEvent_t* g_stage_events = nullptr;
+
+void stage_mark(int i, hipStream_t s) {
+  if (g_stage_events) hipEventRecord(g_stage_events[i], s);
+}
 
 moefp4_status fail(moefp4_status st, const char* fmt, ...) {
   char buf[512];
@@ -188,9 +193,11 @@ moefp4_status moe_fp4_forward(const moefp4_problem* p, const void* x, const uint
   int32_t* sorted = at<int32_t>(workspace, L.sorted);
   int32_t* slot_of = at<int32_t>(workspace, L.slot_of);
   uint32_t* hmax = L.g16_a16 ? at<uint32_t>(workspace, L.hmax) : nullptr;
+  stage_mark(0, stream);
   st = route_into(p, L, topk_ids, counts, offsets, sorted, slot_of, workspace, hmax,
                   L.g16_a16 ? A : 0, stream);
   if (st != MOEFP4_OK) return st;
+  stage_mark(1, stream);
 
   moefp4::FcArgs a;
   memset(&a, 0, sizeof a);
@@ -215,6 +222,7 @@ moefp4_status moe_fp4_forward(const moefp4_problem* p, const void* x, const uint
     a.act = x;
     a.act_sf = x_sf;
     a.h_sf_out = at<uint8_t>(workspace, L.h_sf);
+    stage_mark(2, stream);
     st = hip_status(moefp4::launch_fc1_a8(a, L.nt, L.max_tiles, stream), "fc1");
   } else {
     if (L.g16_a16) {
@@ -230,9 +238,11 @@ moefp4_status moe_fp4_forward(const moefp4_problem* p, const void* x, const uint
     } else {
       a.act = x;
     }
+    stage_mark(2, stream);
     st = hip_status(moefp4::launch_fc1_a16(a, p->gran_k, L.nt, L.max_tiles, stream), "fc1");
   }
   if (st != MOEFP4_OK) return st;
+  stage_mark(3, stream);
 
   // FC2
   a.w = w2;
@@ -252,11 +262,14 @@ moefp4_status moe_fp4_forward(const moefp4_problem* p, const void* x, const uint
                        : moefp4::launch_fc2_a16(a, p->gran_k, L.nt, L.max_tiles, stream),
                   "fc2");
   if (st != MOEFP4_OK) return st;
+  stage_mark(4, stream);
 
   st = hip_status(moefp4::launch_combine(a.y_out, slot_of, topk_w, p->T, p->top_k, p->H, out,
                                          p->out_fmt == MOEFP4_OUT_F32, stream),
                   "combine");
-  return st == MOEFP4_OK ? ok() : st;
+  if (st != MOEFP4_OK) return st;
+  stage_mark(5, stream);
+  return ok();
 }
 
 moefp4_status fp4_requant_gran_k(int64_t E, int64_t N, int64_t K, const uint8_t* src,
@@ -291,6 +304,12 @@ moefp4_status fp4_requant_gran_k(int64_t E, int64_t N, int64_t K, const uint8_t*
   moefp4_status st = hip_status(
       moefp4::launch_requant_g16_g32(src, src_sf, src_gs, dst, dst_sf, E, N, K, stream), "requant");
   return st == MOEFP4_OK ? ok() : st;
+}
+
+moefp4_status moefp4_set_stage_events(hipEvent_t* events, int32_t n) {
+  if (events && n < 6) return fail(MOEFP4_EINVAL, "stage events need an array of 6, got %d", n);
+  g_stage_events = events;
+  return ok();
 }
 
 const char* moefp4_last_error(void) { return g_err.c_str(); }

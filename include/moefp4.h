@@ -139,6 +139,15 @@ moefp4_status fp4_requant_gran_k(int64_t E, int64_t N, int64_t K,
                                  uint8_t* dst, uint8_t* dst_sf, int32_t dst_gran,
                                  hipStream_t stream);
 
+/* Profiling hook.  With events non-NULL and n >= 6, each later
+ * moe_fp4_forward call on this thread records, on its stream, events[0]
+ * before routing, [1] after routing, [2] after the activation preparation
+ * (group16 bf16 path; otherwise right after [1]), [3] after FC1 + SwiGLU,
+ * [4] after FC2 and [5] after the combine -- the caller owns the events
+ * (hipEventCreate) and may change the array between calls.  events = NULL
+ * turns recording off.  n in 1..5 is EINVAL. */
+moefp4_status moefp4_set_stage_events(hipEvent_t* events, int32_t n);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* moefp4_last_error(void);
 
