@@ -246,6 +246,15 @@ def main():
                     "hbm_frac": ab["whole"] / (fwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                     "tflops": flops(cfg) / (fwd_ms * 1e-3) / 1e12},
     }
+    if args.profile:
+        # plain copy of a known size, for scaling the HBM byte counters
+        # (FETCH_SIZE / WRITE_SIZE) of the profiled kernels
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        res["copy_calibration_bytes"] = 1 << 30
     if not args.no_cpu_baseline and not args.profile:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(inp)

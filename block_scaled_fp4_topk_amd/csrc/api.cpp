@@ -180,8 +180,8 @@ moefp4_status moe_fp4_forward(const moefp4_problem* p, const void* x, const uint
   if (L.a8 && !x_sf) return fail(MOEFP4_EINVAL, "FP8 activations need x_sf");
   if (!L.a8 && x_sf) return fail(MOEFP4_EINVAL, "x_sf must be NULL for bfloat16 activations");
   if (misaligned(x, 16) || misaligned(w13, 16) || misaligned(w2, 16) || misaligned(out, 16) ||
-      misaligned(w13_sf, 8) || misaligned(w2_sf, 8) || (x_sf && misaligned(x_sf, 8)))
-    return fail(MOEFP4_EINVAL, "x, w13, w2, out must be 16-byte aligned; scale tensors 8-byte aligned");
+      misaligned(w13_sf, 16) || misaligned(w2_sf, 16) || (x_sf && misaligned(x_sf, 16)))
+    return fail(MOEFP4_EINVAL, "x, x_sf, w13, w13_sf, w2, w2_sf and out must be 16-byte aligned");
   if (!workspace || ws_bytes < L.total)
     return fail(MOEFP4_EWORKSPACE, "workspace of %zu bytes needed, got %zu", L.total,
                 workspace ? ws_bytes : (size_t)0);
@@ -223,7 +223,10 @@ moefp4_status moe_fp4_forward(const moefp4_problem* p, const void* x, const uint
     a.act_sf = x_sf;
     a.h_sf_out = at<uint8_t>(workspace, L.h_sf);
     stage_mark(2, stream);
-    st = hip_status(moefp4::launch_fc1_a8(a, L.nt, L.max_tiles, stream), "fc1");
+    st = hip_status(L.nt == 1 && p->H % 512 == 0
+                        ? moefp4::launch_fc_skinny(a, 2, true, L.max_tiles, stream)
+                        : moefp4::launch_fc1_a8(a, L.nt, L.max_tiles, stream),
+                    "fc1");
   } else {
     if (L.g16_a16) {
       uint16_t* x16 = at<uint16_t>(workspace, L.x16);

@@ -111,7 +111,9 @@ moefp4_status moe_fp4_route(const moefp4_problem* p, const int32_t* topk_ids,
  * FP8 activations with group16 weights return EUNSUPPORTED, like the
  * capability gate on recipe (1, 1, 16) in [P1] / [P2] Current patch scope.
  * x_sf must be NULL for BF16 and non-NULL for FP8.  All pointers device
- * memory; topk_ids [T, k] int32, topk_w [T, k] float32. */
+ * memory; topk_ids [T, k] int32, topk_w [T, k] float32; x, x_sf, the weight
+ * and scale tensors and out 16-byte aligned, the workspace 256-byte aligned
+ * (EINVAL otherwise). */
 moefp4_status moe_fp4_forward(const moefp4_problem* p,
                               const void* x, const uint8_t* x_sf,
                               const int32_t* topk_ids, const float* topk_w,
