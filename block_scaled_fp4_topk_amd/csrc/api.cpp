@@ -286,6 +286,8 @@ moefp4_status fp4_requant_gran_k(int64_t E, int64_t N, int64_t K, const uint8_t*
     return fail(MOEFP4_EUNSUPPORTED, "only group16 -> group32 requantisation is computed, got %d -> %d",
                 src_gran, dst_gran);
   if (K % 32) return fail(MOEFP4_EINVAL, "K must be a multiple of 32, got %lld", (long long)K);
+  if (N * (K / 32) > (int64_t)1 << 30 || E > 65535)
+    return fail(MOEFP4_EUNSUPPORTED, "N*K/32 must be <= 2^30 and E <= 65535");
   const int64_t n = E * N * K;
   if (n == 0) return ok();
   if (!src || !src_sf || !dst || !dst_sf)

@@ -14,59 +14,66 @@ namespace moefp4 {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBlocksPerThread = 4;  // 32-element blocks handled per thread per step
+constexpr int kBlocksPerThread = 4;  // 32-element blocks handled per lane per step
 
+// grid: x = workgroups per expert (grid-stride over the expert's blocks),
+// y = expert.  Each workgroup first tabulates the odd-rounded products of
+// all 256 E4M3 scale bytes with |gs| of its expert.
 __global__ __launch_bounds__(kThreads) void requant_kernel(const uint8_t* src, const uint8_t* src_sf,
                                                            const float* __restrict__ gs,
                                                            uint8_t* dst, uint8_t* __restrict__ dst_sf,
-                                                           int64_t nblk, int64_t blk_per_expert) {
-  const int64_t step = (int64_t)gridDim.x * kThreads * kBlocksPerThread;
-  for (int64_t b0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * kBlocksPerThread; b0 < nblk;
-       b0 += step) {
+                                                           int nb) {
+  __shared__ float2 s_tab[256];
+  __shared__ __attribute__((aligned(16))) uint8_t s_ob[4][64 * kBlocksPerThread];
+  const int e = blockIdx.y;
+  const float g = gs ? gs[e] : 1.0f;
+  const float ag = fabsf(g);
+  const uint32_t gneg = rq::bits(g) >> 31;
+  {
+    float p1, p3;
+    rq::ro_pair(threadIdx.x, ag, p1, p3);
+    s_tab[threadIdx.x] = float2{p1, p3};
+  }
+  __syncthreads();
+  const size_t eb = (size_t)e * (size_t)nb;
+  const uint8_t* sp = src + eb * 16;
+  const uint8_t* ssf = src_sf + eb * 2;
+  uint8_t* dp = dst + eb * 16;
+  uint8_t* dsf = dst_sf + eb;
+  // a wavefront handles 256 consecutive blocks per step; load i of lane l is
+  // block base + 64 i + l, so every load instruction reads 1 KB contiguous
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int step = gridDim.x * kThreads * kBlocksPerThread;
+  for (int base = (blockIdx.x * 4 + wave) * 64 * kBlocksPerThread; base < nb; base += step) {
     uint4 c[kBlocksPerThread];
     uint32_t sf[kBlocksPerThread];
-    float g[kBlocksPerThread];
-    const int nb = nblk - b0 < kBlocksPerThread ? (int)(nblk - b0) : kBlocksPerThread;
-    if (nb == kBlocksPerThread) {
 #pragma unroll
-      for (int i = 0; i < kBlocksPerThread; ++i) c[i] = ld_nt(src + (b0 + i) * 16);
-      const uint2 s = *reinterpret_cast<const uint2*>(src_sf + b0 * 2);
-      sf[0] = s.x & 0xFFFF; sf[1] = s.x >> 16; sf[2] = s.y & 0xFFFF; sf[3] = s.y >> 16;
-    } else {
-      for (int i = 0; i < kBlocksPerThread; ++i) {
-        if (i < nb) {
-          c[i] = *reinterpret_cast<const uint4*>(src + (b0 + i) * 16);
-          sf[i] = *reinterpret_cast<const uint16_t*>(src_sf + (b0 + i) * 2);
-        } else {
-          c[i] = uint4{0, 0, 0, 0};
-          sf[i] = 0;
-        }
-      }
+    for (int i = 0; i < kBlocksPerThread; ++i) {
+      const int b = base + 64 * i + lane;
+      const bool ok = b < nb;
+      c[i] = ok ? ld_nt(sp + (size_t)b * 16) : uint4{0u, 0u, 0u, 0u};
+      sf[i] = ok ? *reinterpret_cast<const uint16_t*>(ssf + (size_t)b * 2) : 0u;
     }
 #pragma unroll
     for (int i = 0; i < kBlocksPerThread; ++i) {
-      const int64_t blk = b0 + i < nblk ? b0 + i : nblk - 1;
-      g[i] = gs ? gs[blk / blk_per_expert] : 1.0f;
-    }
-    uint4 o[kBlocksPerThread];
-    uint32_t ob[kBlocksPerThread];
-#pragma unroll
-    for (int i = 0; i < kBlocksPerThread; ++i) {
+      const int b = base + 64 * i + lane;
+      const float2 ta = s_tab[sf[i] & 0xFF], tb = s_tab[(sf[i] >> 8) & 0xFF];
       const uint32_t in[4] = {c[i].x, c[i].y, c[i].z, c[i].w};
       uint32_t out[4];
-      ob[i] = rq::requant_block(in, sf[i], g[i], out);
-      o[i] = uint4{out[0], out[1], out[2], out[3]};
+      const uint32_t ob = rq::requant_block_tab(in, sf[i], ta.x, ta.y, tb.x, tb.y, gneg, out);
+      if (b < nb) st_nt(dp + (size_t)b * 16, uint4{out[0], out[1], out[2], out[3]});
+      s_ob[wave][64 * i + lane] = (uint8_t)ob;
     }
-    if (nb == kBlocksPerThread) {
-#pragma unroll
-      for (int i = 0; i < kBlocksPerThread; ++i) st_nt(dst + (b0 + i) * 16, o[i]);
-      *reinterpret_cast<uint32_t*>(dst_sf + b0) = ob[0] | (ob[1] << 8) | (ob[2] << 16) | (ob[3] << 24);
+    // the wave's 256 scale bytes leave as one dword per lane (wave-private LDS)
+    __builtin_amdgcn_wave_barrier();
+    const uint32_t w4 = *reinterpret_cast<const uint32_t*>(&s_ob[wave][4 * lane]);
+    if (base + 4 * lane + 3 < nb) {
+      *reinterpret_cast<uint32_t*>(dsf + base + 4 * lane) = w4;
     } else {
-      for (int i = 0; i < nb; ++i) {
-        *reinterpret_cast<uint4*>(dst + (b0 + i) * 16) = o[i];
-        dst_sf[b0 + i] = (uint8_t)ob[i];
-      }
+      for (int j = 0; j < 4; ++j)
+        if (base + 4 * lane + j < nb) dsf[base + 4 * lane + j] = (uint8_t)(w4 >> (8 * j));
     }
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
@@ -75,13 +82,14 @@ __global__ __launch_bounds__(kThreads) void requant_kernel(const uint8_t* src, c
 hipError_t launch_requant_g16_g32(const uint8_t* src, const uint8_t* src_sf, const float* gs,
                                   uint8_t* dst, uint8_t* dst_sf, int64_t E, int64_t N, int64_t K,
                                   hipStream_t s) {
-  const int64_t nblk = E * N * (K / 32);
-  if (nblk <= 0) return hipSuccess;
+  const int64_t nb = N * (K / 32);
+  if (nb <= 0 || E <= 0) return hipSuccess;
   const int64_t per_wg = (int64_t)kThreads * kBlocksPerThread;
-  int64_t grid = (nblk + per_wg - 1) / per_wg;
-  if (grid > 256 * 32) grid = 256 * 32;
-  hipLaunchKernelGGL(requant_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, src, src_sf, gs,
-                     dst, dst_sf, nblk, N * (K / 32));
+  int64_t gx = (nb + per_wg - 1) / per_wg;
+  const int64_t want = (8192 + E - 1) / E;  // ~32 workgroups per CU over the launch
+  if (gx > want) gx = want;
+  hipLaunchKernelGGL(requant_kernel, dim3((unsigned)gx, (unsigned)E), dim3(kThreads), 0, s, src,
+                     src_sf, gs, dst, dst_sf, (int)nb);
   return hipGetLastError();
 }
 

@@ -156,5 +156,92 @@ MOEFP4_HD uint32_t requant_block(const uint32_t c[4], uint32_t sf16, float gs, u
   return (uint32_t)b;
 }
 
+// ---------------------------------------------------------------------------
+// Table-driven form used by the kernel.  Per expert, for every E4M3 byte b:
+//   P1[b] = RO(|E4M3(b)| * |gs|),  P3[b] = RO(3 * |E4M3(b)| * |gs|)
+// (RO = round to odd).  The odd-rounded value of E2M1(m) * |s| * |gs| is then
+// a power-of-two multiple of P1 (m = 1, 2, 4, 6 -> 0.5, 1, 2, 4 x) or of P3
+// (m = 3, 5, 7 -> 0.5, 1, 2 x), so the block maximum and every lookup-table
+// entry come from two table reads and exact scalings.
+
+MOEFP4_HD void ro_pair(uint32_t b, float ag, float& p1, float& p3) {
+  const float s = fabsf(e4m3_f32(b));
+  p1 = mul_ro(s, ag);
+  p3 = mul_ro(3.0f * s, ag);
+}
+
+// odd-rounded E2M1(m) * |s| * |gs| for magnitude code m (0..7), branch-free:
+// m = 1..7 -> {P1/2, P1, P3/2, 2 P1, P3, 4 P1, 2 P3}; m = 0 -> 0
+MOEFP4_HD float ladder(uint32_t m, float p1, float p3) {
+  const uint32_t use3 = (0xA8u >> m) & 1u;                       // m = 3, 5, 7
+  const int k = (int)((0x23120101u >> (4 * m)) & 0xFu) - 1;      // exponent offset
+  const float v = ldexpf(use3 ? p3 : p1, k);
+  return m ? v : 0.0f;
+}
+
+// RNE code of x / 2**(e+1) on the E2M1 grid with saturation at 6 (the
+// semantics of v_cvt_scalef32_pk_fp4_f32 with a power-of-two scale, which
+// the kernel uses; this is the host equivalent).
+MOEFP4_HD uint32_t code_scaled(float x, int e) { return e2m1_code(fminf(ldexpf(x, -e - 1), 6.0f)); }
+
+MOEFP4_HD uint32_t requant_block_tab(const uint32_t c[4], uint32_t sf16, float p1a, float p3a,
+                                     float p1b, float p3b, uint32_t gneg, uint32_t out[4]) {
+  uint32_t lo[4], hi[4];
+  for (int i = 0; i < 4; ++i) {
+    lo[i] = c[i] & 0x07070707u;
+    hi[i] = (c[i] >> 4) & 0x07070707u;
+  }
+  const uint32_t ohl = 0x08040201u, ohh = 0x80402010u;  // one-hot byte 1 << m
+  uint32_t oa = perm8(ohh, ohl, lo[0]) | perm8(ohh, ohl, hi[0]) | perm8(ohh, ohl, lo[1]) |
+                perm8(ohh, ohl, hi[1]);
+  uint32_t ob = perm8(ohh, ohl, lo[2]) | perm8(ohh, ohl, hi[2]) | perm8(ohh, ohl, lo[3]) |
+                perm8(ohh, ohl, hi[3]);
+  oa |= oa >> 16;
+  oa |= oa >> 8;
+  ob |= ob >> 16;
+  ob |= ob >> 8;
+  const uint32_t ma = 31u - (uint32_t)clz32((oa & 0xFFu) | 1u);
+  const uint32_t mb = 31u - (uint32_t)clz32((ob & 0xFFu) | 1u);
+  const uint32_t am = bits(fmaxf(ladder(ma, p1a, p3a), ladder(mb, p1b, p3b)));
+  int b = (int)(am >> 23) - 2 + ((am & 0x7FFFFFu) > 0x400000u ? 1 : 0);
+  b = am == 0 ? 0 : b;
+  b = b < 0 ? 0 : (b > 254 ? 254 : b);
+  const int e = b - 127;
+  const int es = e > 126 ? 126 : e;  // the lookup tables' scaling exponent
+  uint32_t la = 0, ha = 0, lb = 0, hb = 0;
+#if defined(__HIP_DEVICE_COMPILE__)
+  const float sc = fbits((uint32_t)(es + 1 + 127) << 23);
+  la = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(la, p1a, 0.0f, sc, 1);
+  la = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(la, 2.0f * p1a, 0.0f, sc, 2);
+  la = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(la, p3a, 0.0f, sc, 3);
+  ha = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(ha, 4.0f * p1a, 0.0f, sc, 0);
+  ha = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(ha, 2.0f * p3a, 0.0f, sc, 1);
+  ha = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(ha, 8.0f * p1a, 0.0f, sc, 2);
+  ha = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(ha, 4.0f * p3a, 0.0f, sc, 3);
+  lb = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lb, p1b, 0.0f, sc, 1);
+  lb = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lb, 2.0f * p1b, 0.0f, sc, 2);
+  lb = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lb, p3b, 0.0f, sc, 3);
+  hb = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hb, 4.0f * p1b, 0.0f, sc, 0);
+  hb = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hb, 2.0f * p3b, 0.0f, sc, 1);
+  hb = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hb, 8.0f * p1b, 0.0f, sc, 2);
+  hb = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hb, 4.0f * p3b, 0.0f, sc, 3);
+#else
+  la = (code_scaled(p1a, es) << 8) | (code_scaled(2.0f * p1a, es) << 16) | (code_scaled(p3a, es) << 24);
+  ha = code_scaled(4.0f * p1a, es) | (code_scaled(2.0f * p3a, es) << 8) |
+       (code_scaled(8.0f * p1a, es) << 16) | (code_scaled(4.0f * p3a, es) << 24);
+  lb = (code_scaled(p1b, es) << 8) | (code_scaled(2.0f * p1b, es) << 16) | (code_scaled(p3b, es) << 24);
+  hb = code_scaled(4.0f * p1b, es) | (code_scaled(2.0f * p3b, es) << 8) |
+       (code_scaled(8.0f * p1b, es) << 16) | (code_scaled(4.0f * p3b, es) << 24);
+#endif
+  // sign: a negative block scale flips its half, a negative gs the block
+  const uint32_t fa = ((((sf16 >> 7) & 1u) ^ gneg) ? 0x88888888u : 0u);
+  const uint32_t fb = ((((sf16 >> 15) & 1u) ^ gneg) ? 0x88888888u : 0u);
+  out[0] = ((c[0] & 0x88888888u) ^ fa) | perm8(ha, la, lo[0]) | (perm8(ha, la, hi[0]) << 4);
+  out[1] = ((c[1] & 0x88888888u) ^ fa) | perm8(ha, la, lo[1]) | (perm8(ha, la, hi[1]) << 4);
+  out[2] = ((c[2] & 0x88888888u) ^ fb) | perm8(hb, lb, lo[2]) | (perm8(hb, lb, hi[2]) << 4);
+  out[3] = ((c[3] & 0x88888888u) ^ fb) | perm8(hb, lb, lo[3]) | (perm8(hb, lb, hi[3]) << 4);
+  return (uint32_t)b;
+}
+
 }  // namespace rq
 }  // namespace moefp4

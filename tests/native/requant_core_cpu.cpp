@@ -8,7 +8,8 @@
 #include "../../block_scaled_fp4_topk_amd/csrc/requant_core.h"
 
 int main(int argc, char** argv) {
-  if (argc != 3) { fprintf(stderr, "usage: %s in out\n", argv[0]); return 2; }
+  if (argc != 3 && argc != 4) { fprintf(stderr, "usage: %s in out [tab]\n", argv[0]); return 2; }
+  const bool tab = argc == 4;
   FILE* fi = fopen(argv[1], "rb");
   FILE* fo = fopen(argv[2], "wb");
   if (!fi || !fo) return 3;
@@ -19,7 +20,16 @@ int main(int argc, char** argv) {
     memcpy(c, rec, 16);
     sf = rec[16] | (rec[17] << 8);
     memcpy(&gs, rec + 18, 4);
-    uint32_t b = moefp4::rq::requant_block(c, sf, gs, o);
+    uint32_t b;
+    if (tab) {
+      float p1a, p3a, p1b, p3b;
+      moefp4::rq::ro_pair(sf & 0xFF, fabsf(gs), p1a, p3a);
+      moefp4::rq::ro_pair((sf >> 8) & 0xFF, fabsf(gs), p1b, p3b);
+      b = moefp4::rq::requant_block_tab(c, sf, p1a, p3a, p1b, p3b,
+                                        moefp4::rq::bits(gs) >> 31, o);
+    } else {
+      b = moefp4::rq::requant_block(c, sf, gs, o);
+    }
     unsigned char out[17];
     memcpy(out, o, 16);
     out[16] = (unsigned char)b;
