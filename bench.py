@@ -94,6 +94,30 @@ def gpu_forward_into(moe, torch, inp, d, ws, out):
     return ws, out
 
 
+def stage_kernel(cfg, ids, stage):
+    """Symbol of the kernel the library launches for an FC stage at this
+    shape (the dispatch rule of moe_fp4_forward: 16-row expert tiles when an
+    active expert averages at most 16 assignments, else 64-row tiles)."""
+    A = ids.size
+    active = len(np.unique(ids[ids >= 0]))
+    nt = 4 if active and A / active > 16 else 1
+    mode = 2 if cfg.act == "fp8" else (0 if cfg.gran == 16 else 1)
+    if stage == "fc1_swiglu":
+        if nt == 1 and cfg.H % 256 == 0:
+            return f"fc_decode_kernel<{mode}, true>"
+        return f"fc_a8_kernel<{nt}, true>" if mode == 2 else f"fc_a16_kernel<{cfg.gran}, {nt}, true>"
+    if nt == 1 and mode == 0 and cfg.I % 512 == 0:
+        return "fc_skinny_kernel<0, false>"
+    if nt == 1 and mode != 0 and cfg.I % 256 == 0:
+        return f"fc_decode_kernel<{mode}, false>"
+    return f"fc_a8_kernel<{nt}, false>" if mode == 2 else f"fc_a16_kernel<{cfg.gran}, {nt}, false>"
+
+
+def kernel_file_key(symbol):
+    """File-name form of a kernel symbol: fc_decode_kernel<0, true> -> fc_decode_0_true."""
+    return symbol.replace("_kernel<", "_").replace(", ", "_").replace(">", "")
+
+
 def algorithmic_bytes(cfg, ids):
     """Compulsory HBM bytes: the weights (codes, block scales, global scales)
     of every expert that receives at least one token, the activations read
@@ -220,7 +244,8 @@ def main():
     dom = max(("fc1_swiglu", "fc2"), key=lambda s: stage_ms[s])
     dom_bytes = ab["fc1"] if dom == "fc1_swiglu" else ab["fc2"]
     achieved = dom_bytes / (stage_ms[dom] * 1e-3) / 1e9
-    kernel_key = {"fc1_swiglu": "fc1", "fc2": "fc2"}[dom] + ("_a8" if cfg.act == "fp8" else "_a16")
+    kernel = stage_kernel(cfg, inp.topk_ids, dom)
+    kernel_key = kernel_file_key(kernel)
     res = {
         "metric": METRIC,
         "value": cfg.T / (ms_step * 1e-3),
@@ -237,7 +262,7 @@ def main():
         "config": {"workload": WORKLOAD_TEXT[cfg.name], "T": cfg.T, "E": cfg.E, "top_k": cfg.k,
                    "H": cfg.H, "I": cfg.I, "gran_k": cfg.gran, "act": cfg.act,
                    "active_experts": ab["active"], "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": kernel_key, "achieved": achieved,
+        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": pmc_traffic(kernel_key, cfg.name),
                      "algorithmic_bytes_per_launch": dom_bytes, "launch_ms": stage_ms[dom]},

@@ -60,6 +60,9 @@ hipError_t launch_fc2_a8(const FcArgs& a, int nt, int max_tiles, hipStream_t s);
 // group16, 1: bf16 x group32, 2: FP8 x group32.  Needs K % 512 == 0.
 hipError_t launch_fc_skinny(const FcArgs& a, int mode, bool fc1, int max_tiles, hipStream_t s);
 
+// Occupancy-driven decode FC kernels (same modes); needs K % 256 == 0.
+hipError_t launch_fc_decode(const FcArgs& a, int mode, bool fc1, int max_tiles, hipStream_t s);
+
 // out[t, :] = sum_j w[t, j] * y[slot_of[t*k + j], :]  (f32, or rounded to bf16)
 hipError_t launch_combine(const float* y, const int32_t* slot_of, const float* topk_w, int T,
                           int k, int H, void* out, bool out_f32, hipStream_t s);

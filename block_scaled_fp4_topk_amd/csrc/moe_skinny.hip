@@ -35,32 +35,20 @@ constexpr int KC = 512;
 template <int MODE>
 struct Frag {
   uint4 c[4];  // 64 code bytes: piece i = 16 bytes at row offset 16 q + 64 i of the chunk
-  uint4 s;     // MODE 0: 4 x (2 E4M3 bytes) per piece; MODE 1: 16 UE8M0 bytes; MODE 2: 16 UE8M0
+  uint4 s;     // MODE 1/2: the chunk's 16 UE8M0 bytes (MODE 0 scales are staged in LDS)
 };
 
-// Codes: the 4 lanes of a row read 64 contiguous bytes per load instruction;
-// piece i of lane group q holds chunk elements [128 i + 32 q, + 32).
+// Codes: the 4 lanes of a row read 64 contiguous bytes per load instruction
+// (cached loads: the next instruction reads the other half of the same
+// 128-byte lines); piece i of lane group q holds chunk elements
+// [128 i + 32 q, + 32).
 template <int MODE>
 __device__ __forceinline__ void load_frag(Frag<MODE>& f, const uint8_t* rc, const uint8_t* rs,
                                           int k0, int q) {
   const uint8_t* p = rc + (k0 >> 1) + 16 * q;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) f.c[i] = ld_nt(p + 64 * i);
-  if (MODE == 0) {
-    // 32 group16 scale bytes of the chunk; piece i needs groups 8 i + 2 q, + 1
-    const uint4 lo = *reinterpret_cast<const uint4*>(rs + (k0 >> 4));
-    const uint4 hi = *reinterpret_cast<const uint4*>(rs + (k0 >> 4) + 16);
-    const uint32_t d[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-    uint32_t pr[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t w = (q >> 1) ? d[2 * i + 1] : d[2 * i];
-      pr[i] = (q & 1) ? (w >> 16) : (w & 0xFFFFu);
-    }
-    f.s = uint4{pr[0], pr[1], pr[2], pr[3]};
-  } else {
-    f.s = *reinterpret_cast<const uint4*>(rs + (k0 >> 5));
-  }
+  for (int i = 0; i < 4; ++i) f.c[i] = *reinterpret_cast<const uint4*>(p + 64 * i);
+  if (MODE != 0) f.s = *reinterpret_cast<const uint4*>(rs + (k0 >> 5));
 }
 
 __device__ __forceinline__ uint32_t dw(const uint4& v, int r) {
@@ -92,6 +80,8 @@ __global__ __launch_bounds__(256) void fc_skinny_kernel(FcArgs a) {
   __shared__ int s_src[16];
   __shared__ float s_rs[16];
   __shared__ float s_amax[4][16];
+  // MODE 0: the workgroup's 128 rows x 32 group16 scale bytes of a chunk
+  __shared__ __attribute__((aligned(16))) uint8_t s_sc[2][MODE == 0 ? 128 * 32 : 16];
 
   const int tile = blockIdx.x;
   if (tile >= a.ntiles[0]) return;
@@ -145,21 +135,41 @@ __global__ __launch_bounds__(256) void fc_skinny_kernel(FcArgs a) {
   const uint8_t* act = static_cast<const uint8_t*>(a.act);
   const size_t arow = (size_t)K * ESZ;
 
-  auto load_b = [&](int k0, uint4 (&v)[4], uint4& vs) {
-    if (ssrc >= 0) {
-      const uint8_t* p = act + (size_t)ssrc * arow + (size_t)k0 * ESZ + ss * SEGB;
-#pragma unroll
-      for (int i = 0; i < SEGB / 16; ++i) v[i] = *reinterpret_cast<const uint4*>(p + 16 * i);
-      if (MODE == 2 && ss == 0)
-        vs = *reinterpret_cast<const uint4*>(a.act_sf + (size_t)ssrc * (K >> 5) + (k0 >> 5));
+  // Activation staging.  Rows of the tile past the expert's token count load
+  // row 0 instead (no lane-divergent branch around the loads): their MFMA
+  // output columns are never stored.
+  const uint8_t* arow_p = act + (size_t)(ssrc >= 0 ? ssrc : 0) * arow + ss * SEGB;
+  const uint8_t* asf_p =
+      MODE == 2 ? a.act_sf + (size_t)(ssrc >= 0 ? ssrc : 0) * (K >> 5) : nullptr;
+  // MODE 0 scale staging: thread t stages 16 of the 32 scale bytes of WG-local
+  // row t / 2 (FC1: local rows 0..63 gate, 64..127 up; FC2: 128 consecutive)
+  const uint8_t* sc_p = nullptr;
+  if (MODE == 0) {
+    const int lr = tid >> 1;
+    int grow;
+    if (FC1) {
+      const int i0 = blockIdx.y * 64 + (lr & 63);
+      const bool up = lr >= 64;
+      grow = (up != (a.w13_order != 0)) ? a.I + i0 : i0;
     } else {
-#pragma unroll
-      for (int i = 0; i < SEGB / 16; ++i) v[i] = uint4{0u, 0u, 0u, 0u};
-      vs = uint4{0u, 0u, 0u, 0u};
+      grow = blockIdx.y * 128 + lr;
     }
+    sc_p = a.wsf + ((size_t)e * N + grow) * (size_t)(K >> 4) + 16 * (tid & 1);
+  }
+  // WG-local rows of this lane's two tiles (for reading the staged scales)
+  const int lrow0 = FC1 ? wave * 16 + r16 : wave * 32 + r16;
+  const int lrow1 = FC1 ? 64 + wave * 16 + r16 : wave * 32 + 16 + r16;
+  // vs: MODE 2 the row's 16 UE8M0 activation scales of the chunk; MODE 0 the
+  // 16 weight-scale bytes this thread stages
+  auto load_b = [&](int k0, uint4 (&v)[4], uint4& vs) {
+    const uint8_t* p = arow_p + (size_t)k0 * ESZ;
+#pragma unroll
+    for (int i = 0; i < SEGB / 16; ++i) v[i] = *reinterpret_cast<const uint4*>(p + 16 * i);
+    if (MODE == 2) vs = *reinterpret_cast<const uint4*>(asf_p + (k0 >> 5));
+    if (MODE == 0) vs = *reinterpret_cast<const uint4*>(sc_p + (k0 >> 4));
   };
   auto store_b = [&](int buf, uint4 (&v)[4], const uint4& vs) {
-    if (MODE == 0 && !FC1 && ssrc >= 0) {
+    if (MODE == 0 && !FC1) {
       // bf16 h -> fp16 * 2**-p (exact: 8 significant bits, in range)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -178,29 +188,11 @@ __global__ __launch_bounds__(256) void fc_skinny_kernel(FcArgs a) {
 #pragma unroll
     for (int i = 0; i < SEGB / 16; ++i) *reinterpret_cast<uint4*>(d + 16 * i) = v[i];
     if (MODE == 2 && ss == 0) *reinterpret_cast<uint4*>(s_bsf[buf] + sr * 16) = vs;
+    if (MODE == 0) *reinterpret_cast<uint4*>(s_sc[buf] + 16 * tid) = vs;
   };
 
   v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  Frag<MODE> f0, f1, g0, g1;
-  uint4 bv[4];
-  uint4 bvs = {0u, 0u, 0u, 0u};
-  load_frag<MODE>(f0, wc0, ws0, 0, q);
-  load_frag<MODE>(f1, wc1, ws1, 0, q);
-  load_b(0, bv, bvs);
-  store_b(0, bv, bvs);
-  __syncthreads();
-
-  const int nchunks = K / KC;
-  for (int c = 0; c < nchunks; ++c) {
-    const int cur = c & 1;
-    const bool more = c + 1 < nchunks;
-    g0 = f0;
-    g1 = f1;
-    if (more) {
-      load_frag<MODE>(f0, wc0, ws0, (c + 1) * KC, q);
-      load_frag<MODE>(f1, wc1, ws1, (c + 1) * KC, q);
-      load_b((c + 1) * KC, bv, bvs);
-    }
+  auto compute = [&](const Frag<MODE>& g0, const Frag<MODE>& g1, int cur) {
     const uint8_t* brow = s_b[cur] + r16 * ROWB;
     if (MODE == 2) {
 #pragma unroll
@@ -218,12 +210,17 @@ __global__ __launch_bounds__(256) void fc_skinny_kernel(FcArgs a) {
         acc1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A1, B, acc1, 4, 0, 0, sa1, 0, sbb);
       }
     } else {
+      // MODE 0: piece i of lane group q uses the group16 scales 8 i + 2 q, + 1
+      const uint8_t* sc0 = s_sc[cur] + lrow0 * 32 + 2 * q;
+      const uint8_t* sc1 = s_sc[cur] + lrow1 * 32 + 2 * q;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         v2h sp0, sp1;
         if (MODE == 0) {
-          sp0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(dw(g0.s, i), 1.0f, false);
-          sp1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(dw(g1.s, i), 1.0f, false);
+          sp0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(
+              *reinterpret_cast<const uint16_t*>(sc0 + 8 * i), 1.0f, false);
+          sp1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(
+              *reinterpret_cast<const uint16_t*>(sc1 + 8 * i), 1.0f, false);
         }
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
@@ -248,6 +245,30 @@ __global__ __launch_bounds__(256) void fc_skinny_kernel(FcArgs a) {
         }
       }
     }
+  };
+
+  // one chunk ahead: the next chunk's weights and activations are loaded
+  // into registers while the current chunk (in LDS) is multiplied
+  Frag<MODE> f0, f1, g0, g1;
+  uint4 bv[4];
+  uint4 bvs = {0u, 0u, 0u, 0u};
+  load_b(0, bv, bvs);
+  load_frag<MODE>(f0, wc0, ws0, 0, q);
+  load_frag<MODE>(f1, wc1, ws1, 0, q);
+  store_b(0, bv, bvs);
+  __syncthreads();
+  const int nchunks = K / KC;
+  for (int c = 0; c < nchunks; ++c) {
+    const int cur = c & 1;
+    const bool more = c + 1 < nchunks;
+    g0 = f0;
+    g1 = f1;
+    if (more) {
+      load_b((c + 1) * KC, bv, bvs);
+      load_frag<MODE>(f0, wc0, ws0, (c + 1) * KC, q);
+      load_frag<MODE>(f1, wc1, ws1, (c + 1) * KC, q);
+    }
+    compute(g0, g1, cur);
     if (more) store_b(cur ^ 1, bv, bvs);
     __syncthreads();
   }
