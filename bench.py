@@ -102,15 +102,10 @@ def stage_kernel(cfg, ids, stage):
     active = len(np.unique(ids[ids >= 0]))
     nt = 4 if active and A / active > 16 else 1
     mode = 2 if cfg.act == "fp8" else (0 if cfg.gran == 16 else 1)
-    if stage == "fc1_swiglu":
-        if nt == 1 and cfg.H % 256 == 0:
-            return f"fc_decode_kernel<{mode}, true>"
-        return f"fc_a8_kernel<{nt}, true>" if mode == 2 else f"fc_a16_kernel<{cfg.gran}, {nt}, true>"
-    if nt == 1 and mode == 0 and cfg.I % 512 == 0:
-        return "fc_skinny_kernel<0, false>"
-    if nt == 1 and mode != 0 and cfg.I % 256 == 0:
-        return f"fc_decode_kernel<{mode}, false>"
-    return f"fc_a8_kernel<{nt}, false>" if mode == 2 else f"fc_a16_kernel<{cfg.gran}, {nt}, false>"
+    if nt == 1:
+        return f"fc_decode_kernel<{mode}, {'true' if stage == 'fc1_swiglu' else 'false'}>"
+    fc1 = "true" if stage == "fc1_swiglu" else "false"
+    return f"fc_a8_kernel<{nt}, {fc1}>" if mode == 2 else f"fc_a16_kernel<{cfg.gran}, {nt}, {fc1}>"
 
 
 def kernel_file_key(symbol):

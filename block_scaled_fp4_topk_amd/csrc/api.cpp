@@ -223,7 +223,7 @@ moefp4_status moe_fp4_forward(const moefp4_problem* p, const void* x, const uint
     a.act_sf = x_sf;
     a.h_sf_out = at<uint8_t>(workspace, L.h_sf);
     stage_mark(2, stream);
-    st = hip_status(L.nt == 1 && p->H % 256 == 0
+    st = hip_status(L.nt == 1
                         ? moefp4::launch_fc_decode(a, 2, true, L.max_tiles, stream)
                         : moefp4::launch_fc1_a8(a, L.nt, L.max_tiles, stream),
                     "fc1");
@@ -242,7 +242,7 @@ moefp4_status moe_fp4_forward(const moefp4_problem* p, const void* x, const uint
       a.act = x;
     }
     stage_mark(2, stream);
-    st = hip_status(L.nt == 1 && p->H % 256 == 0
+    st = hip_status(L.nt == 1
                         ? moefp4::launch_fc_decode(a, p->gran_k == 16 ? 0 : 1, true, L.max_tiles, stream)
                         : moefp4::launch_fc1_a16(a, p->gran_k, L.nt, L.max_tiles, stream),
                     "fc1");
@@ -265,11 +265,7 @@ moefp4_status moe_fp4_forward(const moefp4_problem* p, const void* x, const uint
   a.h_sf_out = nullptr;
   a.y_out = at<float>(workspace, L.y);
   const int mode = L.a8 ? 2 : (p->gran_k == 16 ? 0 : 1);
-  // decode-shaped FC2: group16 weights use the chunk-prefetch kernel with the
-  // scales staged in LDS, the group32 forms the occupancy-driven kernel
-  st = hip_status(L.nt == 1 && mode == 0 && p->I % 512 == 0
-                      ? moefp4::launch_fc_skinny(a, mode, false, L.max_tiles, stream)
-                  : L.nt == 1 && mode != 0 && p->I % 256 == 0
+  st = hip_status(L.nt == 1
                       ? moefp4::launch_fc_decode(a, mode, false, L.max_tiles, stream)
                   : L.a8 ? moefp4::launch_fc2_a8(a, L.nt, L.max_tiles, stream)
                              : moefp4::launch_fc2_a16(a, p->gran_k, L.nt, L.max_tiles, stream),

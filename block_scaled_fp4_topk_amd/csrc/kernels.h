@@ -56,11 +56,9 @@ hipError_t launch_fc2_a16(const FcArgs& a, int gran, int nt, int max_tiles, hipS
 hipError_t launch_fc1_a8(const FcArgs& a, int nt, int max_tiles, hipStream_t s);
 hipError_t launch_fc2_a8(const FcArgs& a, int nt, int max_tiles, hipStream_t s);
 
-// Decode-shaped (tile of <= 16 activation rows) FC kernels; mode 0: bf16 x
-// group16, 1: bf16 x group32, 2: FP8 x group32.  Needs K % 512 == 0.
-hipError_t launch_fc_skinny(const FcArgs& a, int mode, bool fc1, int max_tiles, hipStream_t s);
-
-// Occupancy-driven decode FC kernels (same modes); needs K % 256 == 0.
+// Decode-shaped FC kernels (expert tiles of <= 16 activation rows); mode 0:
+// bf16 x group16, 1: bf16 x group32, 2: FP8 x group32.  Needs K % 256 == 0,
+// I % 64 == 0 (FC1) and H % 128 == 0 (FC2).
 hipError_t launch_fc_decode(const FcArgs& a, int mode, bool fc1, int max_tiles, hipStream_t s);
 
 // out[t, :] = sum_j w[t, j] * y[slot_of[t*k + j], :]  (f32, or rounded to bf16)

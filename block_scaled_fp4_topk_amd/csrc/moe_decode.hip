@@ -27,6 +27,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <type_traits>
+
 namespace moefp4 {
 
 namespace {
@@ -57,8 +59,13 @@ __global__ __launch_bounds__(256, 8) void fc_decode_kernel(FcArgs a) {
   constexpr int ESZ = MODE == 2 ? 1 : 2;          // activation element bytes
   constexpr int ROWB = KC * ESZ + 16;             // staged row stride (bytes)
   constexpr int SEGB = KC * ESZ / 16;             // bytes staged per thread (32 or 16)
+  constexpr int SCB = MODE == 0 ? KC / 16 : KC / 32;  // weight-scale bytes per row per chunk
+  constexpr int SCROW = 4 * SCB + (MODE == 0 ? 16 : 8);  // staged scale row stride (bytes)
+  using ScPiece = typename std::conditional<MODE == 0, uint4, uint2>::type;
   __shared__ __attribute__((aligned(16))) uint8_t s_b[16 * ROWB];
   __shared__ __attribute__((aligned(16))) uint8_t s_bsf[16 * 8];
+  // weight scales of 4 chunks for the workgroup's 128 rows (padded rows)
+  __shared__ __attribute__((aligned(16))) uint8_t s_sc[128 * SCROW];
   __shared__ int s_src[16];
   __shared__ float s_rs[16];
   __shared__ float s_amax[4][16];
@@ -84,8 +91,6 @@ __global__ __launch_bounds__(256, 8) void fc_decode_kernel(FcArgs a) {
   const size_t rb = (size_t)(K >> 1), sb = (size_t)(K / (MODE == 0 ? 16 : 32));
   const uint8_t* wc0 = a.w + ((size_t)e * N + row0) * rb + 16 * q;
   const uint8_t* wc1 = a.w + ((size_t)e * N + row1) * rb + 16 * q;
-  const uint8_t* ws0 = a.wsf + ((size_t)e * N + row0) * sb;
-  const uint8_t* ws1 = a.wsf + ((size_t)e * N + row1) * sb;
 
   if (tid < 16) {
     const int m = m0 + tid;
@@ -108,7 +113,9 @@ __global__ __launch_bounds__(256, 8) void fc_decode_kernel(FcArgs a) {
   }
   __syncthreads();
 
-  // staging role: row sr, segment ss
+  // staging role: row sr, segment ss.  Rows past the expert's token count are
+  // not loaded: their LDS contents only reach MFMA output columns that are
+  // never stored.
   const int sr = tid >> 4, ss = tid & 15;
   const int ssrc = s_src[sr];
   const float sinv = 1.0f / s_rs[sr];
@@ -116,35 +123,54 @@ __global__ __launch_bounds__(256, 8) void fc_decode_kernel(FcArgs a) {
   const uint8_t* arow_p = act + (size_t)(ssrc >= 0 ? ssrc : 0) * ((size_t)K * ESZ) + ss * SEGB;
   const uint8_t* asf_p = MODE == 2 ? a.act_sf + (size_t)(ssrc >= 0 ? ssrc : 0) * (K >> 5) : nullptr;
 
+  // Weight-scale staging: once per group of 4 chunks the workgroup's 128 rows
+  // x 4 chunks of scale bytes go to LDS.  Thread t loads the chunk (t & 3)
+  // piece of WG-local rows t / 4 and 64 + t / 4, so the 4 threads of a row
+  // read its 4 * SCB contiguous bytes.  WG-local rows: FC1 0..63 gate and
+  // 64..127 up of the 64 outputs; FC2 128 consecutive rows.
+  const int sq = tid & 3, slr = tid >> 2;
+  const uint8_t* sc_src[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int lr = slr + 64 * h;
+    int grow;
+    if (FC1) {
+      const int i0 = blockIdx.x * 64 + (lr & 63);
+      grow = ((lr >= 64) != (a.w13_order != 0)) ? a.I + i0 : i0;
+    } else {
+      grow = blockIdx.x * 128 + lr;
+    }
+    sc_src[h] = a.wsf + ((size_t)e * N + grow) * sb + sq * SCB;
+  }
+  // this lane's rows in the staged scales
+  const int lrow0 = FC1 ? wave * 16 + r16 : wave * 32 + r16;
+  const int lrow1 = FC1 ? 64 + wave * 16 + r16 : wave * 32 + 16 + r16;
+
   v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   const int nchunks = K / KC;
   for (int c = 0; c < nchunks; ++c) {
     const int k0 = c * KC;
     // activation segment of this thread
-    uint4 bv0 = *reinterpret_cast<const uint4*>(arow_p + (size_t)k0 * ESZ);
-    uint4 bv1 = SEGB == 32 ? *reinterpret_cast<const uint4*>(arow_p + (size_t)k0 * ESZ + 16) : uint4{0u, 0u, 0u, 0u};
+    uint4 bv0 = {0u, 0u, 0u, 0u}, bv1 = {0u, 0u, 0u, 0u};
     uint2 bsf = {0u, 0u};
-    if (MODE == 2) bsf = *reinterpret_cast<const uint2*>(asf_p + (k0 >> 5));
+    if (ssrc >= 0) {
+      bv0 = *reinterpret_cast<const uint4*>(arow_p + (size_t)k0 * ESZ);
+      if (SEGB == 32) bv1 = *reinterpret_cast<const uint4*>(arow_p + (size_t)k0 * ESZ + 16);
+      if (MODE == 2) bsf = *reinterpret_cast<const uint2*>(asf_p + (k0 >> 5));
+    }
+    // weight scales of the next 4 chunks
+    const bool sgroup = (c & 3) == 0;
+    ScPiece sp0 = {}, sp1 = {};
+    if (sgroup && c + sq < nchunks) {
+      const size_t off = (size_t)(k0 / KC) * SCB;
+      sp0 = *reinterpret_cast<const ScPiece*>(sc_src[0] + off);
+      sp1 = *reinterpret_cast<const ScPiece*>(sc_src[1] + off);
+    }
     // weights: pieces i = 0, 1 of 16 bytes at row offset 16 q + 64 i
     const uint4 c00 = *reinterpret_cast<const uint4*>(wc0 + (k0 >> 1));
     const uint4 c01 = *reinterpret_cast<const uint4*>(wc0 + (k0 >> 1) + 64);
     const uint4 c10 = *reinterpret_cast<const uint4*>(wc1 + (k0 >> 1));
     const uint4 c11 = *reinterpret_cast<const uint4*>(wc1 + (k0 >> 1) + 64);
-    uint32_t s0a, s0b, s1a, s1b;  // scales of the two pieces of the two tiles
-    if (MODE == 0) {
-      // piece i needs the group16 scales 8 i + 2 q and + 1
-      const uint8_t* p0 = ws0 + (k0 >> 4) + 2 * q;
-      const uint8_t* p1 = ws1 + (k0 >> 4) + 2 * q;
-      s0a = *reinterpret_cast<const uint16_t*>(p0);
-      s0b = *reinterpret_cast<const uint16_t*>(p0 + 8);
-      s1a = *reinterpret_cast<const uint16_t*>(p1);
-      s1b = *reinterpret_cast<const uint16_t*>(p1 + 8);
-    } else {
-      // the chunk's 8 UE8M0 bytes (piece / step i uses byte 4 i + q)
-      const uint2 v0 = *reinterpret_cast<const uint2*>(ws0 + (k0 >> 5));
-      const uint2 v1 = *reinterpret_cast<const uint2*>(ws1 + (k0 >> 5));
-      s0a = v0.x; s0b = v0.y; s1a = v1.x; s1b = v1.y;
-    }
     if (MODE == 0 && !FC1) {
       // bf16 h -> fp16 * 2**-p (exact: 8 significant bits, in range)
       uint32_t w[8] = {bv0.x, bv0.y, bv0.z, bv0.w, bv1.x, bv1.y, bv1.z, bv1.w};
@@ -161,7 +187,30 @@ __global__ __launch_bounds__(256, 8) void fc_decode_kernel(FcArgs a) {
     *reinterpret_cast<uint4*>(d) = bv0;
     if (SEGB == 32) *reinterpret_cast<uint4*>(d + 16) = bv1;
     if (MODE == 2 && ss == 0) *reinterpret_cast<uint2*>(s_bsf + sr * 8) = bsf;
+    if (sgroup) {
+      *reinterpret_cast<ScPiece*>(s_sc + slr * SCROW + sq * SCB) = sp0;
+      *reinterpret_cast<ScPiece*>(s_sc + (64 + slr) * SCROW + sq * SCB) = sp1;
+    }
     __syncthreads();
+
+    // scales of the two pieces of the two tiles
+    uint32_t s0a, s0b, s1a, s1b;
+    {
+      const uint8_t* p0 = s_sc + lrow0 * SCROW + (c & 3) * SCB;
+      const uint8_t* p1 = s_sc + lrow1 * SCROW + (c & 3) * SCB;
+      if (MODE == 0) {
+        // piece i needs the group16 scales 8 i + 2 q and + 1
+        s0a = *reinterpret_cast<const uint16_t*>(p0 + 2 * q);
+        s0b = *reinterpret_cast<const uint16_t*>(p0 + 8 + 2 * q);
+        s1a = *reinterpret_cast<const uint16_t*>(p1 + 2 * q);
+        s1b = *reinterpret_cast<const uint16_t*>(p1 + 8 + 2 * q);
+      } else {
+        // the chunk's 8 UE8M0 bytes (piece / step i uses byte 4 i + q)
+        const uint2 v0 = *reinterpret_cast<const uint2*>(p0);
+        const uint2 v1 = *reinterpret_cast<const uint2*>(p1);
+        s0a = v0.x; s0b = v0.y; s1a = v1.x; s1b = v1.y;
+      }
+    }
 
     const uint8_t* brow = s_b + r16 * ROWB;
     if (MODE == 2) {
