@@ -99,7 +99,7 @@ moefp4_status plan(const moefp4_problem* p, Layout* L) {
   L->tiles = take((size_t)L->max_tiles * 8);
   L->ntiles = take(4);
   L->act_scale = take(L->g16_a16 ? T * 4 : 0);
-  L->x16 = take(L->g16_a16 ? T * H * 2 : 0);
+  L->x16 = take(L->g16_a16 && L->nt != 1 ? T * H * 2 : 0);
   L->hmax = take(L->g16_a16 ? A * 4 : 0);
   L->h = take(L->a8 ? A * I : A * I * 2);
   L->h_sf = take(L->a8 ? A * (I / 32) : 0);
@@ -122,7 +122,8 @@ moefp4_status hip_status(hipError_t e, const char* what) {
 
 moefp4_status route_into(const moefp4_problem* p, const Layout& L, const int32_t* ids,
                          int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* slot_of,
-                         void* ws, uint32_t* zero_words, int n_zero, hipStream_t s) {
+                         void* ws, uint32_t* zero_words, int n_zero, const void* x, float* row_scale,
+                         hipStream_t s) {
   moefp4::RouteOut o;
   o.counts = counts;
   o.offsets = offsets;
@@ -133,6 +134,10 @@ moefp4_status route_into(const moefp4_problem* p, const Layout& L, const int32_t
   o.flags = at<int32_t>(ws, L.flags);
   o.zero_words = zero_words;
   o.n_zero = n_zero;
+  o.x = static_cast<const uint16_t*>(x);
+  o.T = p->T;
+  o.H = p->H;
+  o.row_scale = row_scale;
   return hip_status(moefp4::launch_route(ids, p->T * p->top_k, p->E, L.tile_m, o, s), "route");
 }
 
@@ -162,7 +167,7 @@ moefp4_status moe_fp4_route(const moefp4_problem* p, const int32_t* topk_ids, in
     return fail(MOEFP4_EWORKSPACE, "workspace of %zu bytes needed, got %zu", L.total,
                 workspace ? ws_bytes : (size_t)0);
   st = route_into(p, L, topk_ids, counts, offsets, sorted_assign, slot_of, workspace, nullptr, 0,
-                  stream);
+                  nullptr, nullptr, stream);
   return st == MOEFP4_OK ? ok() : st;
 }
 
@@ -194,8 +199,12 @@ moefp4_status moe_fp4_forward(const moefp4_problem* p, const void* x, const uint
   int32_t* slot_of = at<int32_t>(workspace, L.slot_of);
   uint32_t* hmax = L.g16_a16 ? at<uint32_t>(workspace, L.hmax) : nullptr;
   stage_mark(0, stream);
+  // group16 weights with bf16 x on 16-row tiles: the route launch also
+  // computes the per-token fp16 staging scales, and FC1 converts while staging
+  const bool stage_f16 = L.g16_a16 && L.nt == 1;
+  float* xs = L.g16_a16 ? at<float>(workspace, L.act_scale) : nullptr;
   st = route_into(p, L, topk_ids, counts, offsets, sorted, slot_of, workspace, hmax,
-                  L.g16_a16 ? A : 0, stream);
+                  L.g16_a16 ? A : 0, stage_f16 ? x : nullptr, stage_f16 ? xs : nullptr, stream);
   if (st != MOEFP4_OK) return st;
   stage_mark(1, stream);
 
@@ -228,9 +237,12 @@ moefp4_status moe_fp4_forward(const moefp4_problem* p, const void* x, const uint
                         : moefp4::launch_fc1_a8(a, L.nt, L.max_tiles, stream),
                     "fc1");
   } else {
-    if (L.g16_a16) {
+    if (stage_f16) {
+      a.act = x;
+      a.act_scale = xs;
+      a.hmax_out = hmax;
+    } else if (L.g16_a16) {
       uint16_t* x16 = at<uint16_t>(workspace, L.x16);
-      float* xs = at<float>(workspace, L.act_scale);
       st = hip_status(moefp4::launch_rows_to_f16(static_cast<const uint16_t*>(x), p->T, p->H, x16, xs,
                                                  stream),
                       "rows_to_f16");

@@ -21,6 +21,12 @@ struct RouteOut {
   int32_t* flags;          // [1] dropped assignments
   uint32_t* zero_words;    // optional [n_zero] words cleared by the route kernel
   int n_zero;
+  // optional: per-token fp16 staging scale of bf16 rows x [T, H] (row_scale
+  // null: not computed); row_scale[t] = 2**p_t with p_t chosen so the row
+  // maximum times 2**-p_t lies in [2**14, 2**15)
+  const uint16_t* x;
+  int T, H;
+  float* row_scale;
 };
 
 hipError_t launch_route(const int32_t* topk_ids, int A, int E, int tile_m, const RouteOut& o,

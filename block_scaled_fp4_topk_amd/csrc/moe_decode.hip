@@ -34,6 +34,9 @@ namespace moefp4 {
 namespace {
 
 constexpr int KC = 256;
+// chunks per weight-scale staging group: group16 scales (16 B per row per
+// chunk) are staged 8 chunks = one full 128-byte line per row at a time,
+// group32 scales 4 chunks (measured best for each)
 
 __device__ __forceinline__ uint32_t dw(const uint4& v, int r) {
   return r == 0 ? v.x : r == 1 ? v.y : r == 2 ? v.z : v.w;
@@ -60,7 +63,8 @@ __global__ __launch_bounds__(256, 8) void fc_decode_kernel(FcArgs a) {
   constexpr int ROWB = KC * ESZ + 16;             // staged row stride (bytes)
   constexpr int SEGB = KC * ESZ / 16;             // bytes staged per thread (32 or 16)
   constexpr int SCB = MODE == 0 ? KC / 16 : KC / 32;  // weight-scale bytes per row per chunk
-  constexpr int SCROW = 4 * SCB + (MODE == 0 ? 16 : 8);  // staged scale row stride (bytes)
+  constexpr int SG = MODE == 0 ? 8 : 4;
+  constexpr int SCROW = SG * SCB + (MODE == 0 ? 16 : 8);  // staged scale row stride (bytes)
   using ScPiece = typename std::conditional<MODE == 0, uint4, uint2>::type;
   __shared__ __attribute__((aligned(16))) uint8_t s_b[16 * ROWB];
   __shared__ __attribute__((aligned(16))) uint8_t s_bsf[16 * 8];
@@ -123,16 +127,17 @@ __global__ __launch_bounds__(256, 8) void fc_decode_kernel(FcArgs a) {
   const uint8_t* arow_p = act + (size_t)(ssrc >= 0 ? ssrc : 0) * ((size_t)K * ESZ) + ss * SEGB;
   const uint8_t* asf_p = MODE == 2 ? a.act_sf + (size_t)(ssrc >= 0 ? ssrc : 0) * (K >> 5) : nullptr;
 
-  // Weight-scale staging: once per group of 4 chunks the workgroup's 128 rows
-  // x 4 chunks of scale bytes go to LDS.  Thread t loads the chunk (t & 3)
-  // piece of WG-local rows t / 4 and 64 + t / 4, so the 4 threads of a row
-  // read its 4 * SCB contiguous bytes.  WG-local rows: FC1 0..63 gate and
-  // 64..127 up of the 64 outputs; FC2 128 consecutive rows.
-  const int sq = tid & 3, slr = tid >> 2;
-  const uint8_t* sc_src[2];
+  // Weight-scale staging: once per group of SG chunks the workgroup's 128
+  // rows x SG chunks of scale bytes go to LDS.  Thread t loads the chunk
+  // (t % SG) piece of WG-local rows t / SG + (256 / SG) h, h < SG / 2, so the
+  // SG threads of a row read its SG * SCB contiguous bytes.  WG-local rows:
+  // FC1 0..63 gate and 64..127 up of the 64 outputs; FC2 128 consecutive rows.
+  constexpr int NH = SG / 2;  // rows staged per thread
+  const int sq = tid % SG, slr = tid / SG;
+  const uint8_t* sc_src[NH];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int lr = slr + 64 * h;
+  for (int h = 0; h < NH; ++h) {
+    const int lr = slr + (256 / SG) * h;
     int grow;
     if (FC1) {
       const int i0 = blockIdx.x * 64 + (lr & 63);
@@ -159,20 +164,22 @@ __global__ __launch_bounds__(256, 8) void fc_decode_kernel(FcArgs a) {
       if (MODE == 2) bsf = *reinterpret_cast<const uint2*>(asf_p + (k0 >> 5));
     }
     // weight scales of the next 4 chunks
-    const bool sgroup = (c & 3) == 0;
-    ScPiece sp0 = {}, sp1 = {};
+    const bool sgroup = (c % SG) == 0;
+    ScPiece sp[NH];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) sp[h] = ScPiece{};
     if (sgroup && c + sq < nchunks) {
       const size_t off = (size_t)(k0 / KC) * SCB;
-      sp0 = *reinterpret_cast<const ScPiece*>(sc_src[0] + off);
-      sp1 = *reinterpret_cast<const ScPiece*>(sc_src[1] + off);
+#pragma unroll
+      for (int h = 0; h < NH; ++h) sp[h] = *reinterpret_cast<const ScPiece*>(sc_src[h] + off);
     }
     // weights: pieces i = 0, 1 of 16 bytes at row offset 16 q + 64 i
     const uint4 c00 = *reinterpret_cast<const uint4*>(wc0 + (k0 >> 1));
     const uint4 c01 = *reinterpret_cast<const uint4*>(wc0 + (k0 >> 1) + 64);
     const uint4 c10 = *reinterpret_cast<const uint4*>(wc1 + (k0 >> 1));
     const uint4 c11 = *reinterpret_cast<const uint4*>(wc1 + (k0 >> 1) + 64);
-    if (MODE == 0 && !FC1) {
-      // bf16 h -> fp16 * 2**-p (exact: 8 significant bits, in range)
+    if (MODE == 0) {
+      // bf16 x or h -> fp16 * 2**-p (exact: 8 significant bits, in range)
       uint32_t w[8] = {bv0.x, bv0.y, bv0.z, bv0.w, bv1.x, bv1.y, bv1.z, bv1.w};
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -188,16 +195,17 @@ __global__ __launch_bounds__(256, 8) void fc_decode_kernel(FcArgs a) {
     if (SEGB == 32) *reinterpret_cast<uint4*>(d + 16) = bv1;
     if (MODE == 2 && ss == 0) *reinterpret_cast<uint2*>(s_bsf + sr * 8) = bsf;
     if (sgroup) {
-      *reinterpret_cast<ScPiece*>(s_sc + slr * SCROW + sq * SCB) = sp0;
-      *reinterpret_cast<ScPiece*>(s_sc + (64 + slr) * SCROW + sq * SCB) = sp1;
+#pragma unroll
+      for (int h = 0; h < NH; ++h)
+        *reinterpret_cast<ScPiece*>(s_sc + (slr + (256 / SG) * h) * SCROW + sq * SCB) = sp[h];
     }
     __syncthreads();
 
     // scales of the two pieces of the two tiles
     uint32_t s0a, s0b, s1a, s1b;
     {
-      const uint8_t* p0 = s_sc + lrow0 * SCROW + (c & 3) * SCB;
-      const uint8_t* p1 = s_sc + lrow1 * SCROW + (c & 3) * SCB;
+      const uint8_t* p0 = s_sc + lrow0 * SCROW + (c % SG) * SCB;
+      const uint8_t* p1 = s_sc + lrow1 * SCROW + (c % SG) * SCB;
       if (MODE == 0) {
         // piece i needs the group16 scales 8 i + 2 q and + 1
         s0a = *reinterpret_cast<const uint16_t*>(p0 + 2 * q);

@@ -47,6 +47,38 @@ __device__ int block_exclusive_scan(int v, int* s_tmp, int* total) {
   return before + x - v;
 }
 
+// Power-of-two fp16 staging exponent of a bf16 row: p = floor(log2(max |x|))
+// - 14, so that max * 2**-p lies in [2**14, 2**15) (bf16's 8 significant bits
+// then fit fp16 exactly down to 2**-24 of the scaled range).
+__device__ __forceinline__ int row_exponent(uint32_t maxbits) {
+  const int p = maxbits ? (int)(maxbits >> 23) - 127 - 14 : 0;
+  return p < -110 ? -110 : p;
+}
+
+// One wavefront per row: the row's largest |x| (compared as bit patterns).
+__device__ void row_scales(const RouteOut& o) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int t = (blockIdx.x - 1) * kRouteWaves + wave; t < o.T; t += (gridDim.x - 1) * kRouteWaves) {
+    const uint16_t* row = o.x + (size_t)t * o.H;
+    uint32_t m = 0;
+    for (int i = lane * 8; i < o.H; i += 512) {
+      const uint4 v = *reinterpret_cast<const uint4*>(row + i);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t lo = (w[j] & 0x7FFFu) << 16, hi = (w[j] & 0x7FFF0000u);
+        m = lo > m ? lo : m;
+        m = hi > m ? hi : m;
+      }
+    }
+    for (int d = 32; d >= 1; d >>= 1) {
+      const uint32_t y = __shfl_xor(m, d, 64);
+      m = y > m ? y : m;
+    }
+    if (lane == 0) o.row_scale[t] = __builtin_ldexpf(1.0f, row_exponent(m));
+  }
+}
+
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t* __restrict__ ids,
                                                               int A, int E, int tile_m,
                                                               RouteOut o) {
@@ -57,6 +89,11 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t* __r
   __shared__ int s_tmp[128];
   __shared__ int s_drop;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // workgroups past the first compute the per-row staging scales instead
+  if (blockIdx.x > 0) {
+    row_scales(o);
+    return;
+  }
 
   for (int i = tid; i < o.n_zero; i += kRouteThreads) o.zero_words[i] = 0u;
   for (int e = tid; e < E; e += kRouteThreads) s_cnt[e] = 0;
@@ -153,9 +190,7 @@ __global__ __launch_bounds__(256) void rows_to_f16_kernel(const uint16_t* __rest
   __syncthreads();
   m = s_max[0];
   for (int w = 1; w < 4; ++w) m = s_max[w] > m ? s_max[w] : m;
-  // p = floor(log2(max)) - 14 so that max * 2**-p lies in [2**14, 2**15)
-  int p = m ? (int)(m >> 23) - 127 - 14 : 0;
-  p = p < -110 ? -110 : p;
+  const int p = row_exponent(m);
   const float inv = __builtin_ldexpf(1.0f, -p);
   uint16_t* orow = x16 + (size_t)t * H;
   for (int i = threadIdx.x; i < H; i += 256) {
@@ -170,8 +205,13 @@ __global__ __launch_bounds__(256) void rows_to_f16_kernel(const uint16_t* __rest
 hipError_t launch_route(const int32_t* topk_ids, int A, int E, int tile_m, const RouteOut& o,
                         hipStream_t s) {
   const size_t lds = (size_t)(E + kRouteWaves * E) * sizeof(int);
-  hipLaunchKernelGGL(route_kernel, dim3(1), dim3(kRouteThreads), lds, s, topk_ids, A, E, tile_m,
-                     o);
+  int scale_blocks = 0;
+  if (o.row_scale && o.T > 0) {
+    scale_blocks = (o.T + kRouteWaves - 1) / kRouteWaves;
+    scale_blocks = scale_blocks > 256 ? 256 : scale_blocks;
+  }
+  hipLaunchKernelGGL(route_kernel, dim3(1 + scale_blocks), dim3(kRouteThreads), lds, s, topk_ids, A,
+                     E, tile_m, o);
   return hipGetLastError();
 }
 
