@@ -97,11 +97,16 @@ def gpu_forward_into(moe, torch, inp, d, ws, out):
 def stage_kernel(cfg, ids, stage):
     """Symbol of the kernel the library launches for an FC stage at this
     shape (the dispatch rule of moe_fp4_forward: 16-row expert tiles when an
-    active expert averages at most 16 assignments, else 64-row tiles)."""
+    active expert averages at most 16 assignments, else 128-row tiles for the
+    FP8 x FP4 GEMM or 64-row tiles)."""
     A = ids.size
     active = len(np.unique(ids[ids >= 0]))
-    nt = 4 if active and A / active > 16 else 1
     mode = 2 if cfg.act == "fp8" else (0 if cfg.gran == 16 else 1)
+    gemm_ok = (mode == 2 and cfg.I % 128 == 0 and cfg.H % 256 == 0 and cfg.T * cfg.H < 2**31
+               and A * cfg.I < 2**31 and cfg.I * cfg.H < 2**31)
+    nt = (8 if gemm_ok else 4) if active and A / active > 16 else 1
+    if nt == 8:
+        return f"fc_gemm_a8_kernel<{'true' if stage == 'fc1_swiglu' else 'false'}>"
     if nt == 1:
         return f"fc_decode_kernel<{mode}, {'true' if stage == 'fc1_swiglu' else 'false'}>"
     fc1 = "true" if stage == "fc1_swiglu" else "false"

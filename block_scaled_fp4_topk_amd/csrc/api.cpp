@@ -86,7 +86,12 @@ moefp4_status plan(const moefp4_problem* p, Layout* L) {
   L->g16_a16 = !L->a8 && p->gran_k == 16;
   const size_t active = A < E ? A : E;
   const double avg = active ? (double)A / (double)active : 0.0;
-  L->nt = avg > 16.0 ? 4 : 1;
+  // 16-row tiles for decode-shaped routing; 128-row tiles for the FP8 x FP4
+  // prefill GEMM (needs 32-bit row offsets and its row-block shapes); else
+  // 64-row tiles
+  const bool gemm_ok = L->a8 && I % 128 == 0 && H % 256 == 0 && T * H < (1ull << 31) &&
+                       A * I < (1ull << 31) && I * H < (1ull << 31);
+  L->nt = avg > 16.0 ? (gemm_ok ? 8 : 4) : 1;
   L->tile_m = 16 * L->nt;
   L->max_tiles = (int)(A / L->tile_m + active);
   size_t o = 0;
@@ -232,8 +237,8 @@ moefp4_status moe_fp4_forward(const moefp4_problem* p, const void* x, const uint
     a.act_sf = x_sf;
     a.h_sf_out = at<uint8_t>(workspace, L.h_sf);
     stage_mark(2, stream);
-    st = hip_status(L.nt == 1
-                        ? moefp4::launch_fc_decode(a, 2, true, L.max_tiles, stream)
+    st = hip_status(L.nt == 1   ? moefp4::launch_fc_decode(a, 2, true, L.max_tiles, stream)
+                    : L.nt == 8 ? moefp4::launch_fc_gemm_a8(a, true, L.max_tiles, stream)
                         : moefp4::launch_fc1_a8(a, L.nt, L.max_tiles, stream),
                     "fc1");
   } else {
@@ -277,8 +282,8 @@ moefp4_status moe_fp4_forward(const moefp4_problem* p, const void* x, const uint
   a.h_sf_out = nullptr;
   a.y_out = at<float>(workspace, L.y);
   const int mode = L.a8 ? 2 : (p->gran_k == 16 ? 0 : 1);
-  st = hip_status(L.nt == 1
-                      ? moefp4::launch_fc_decode(a, mode, false, L.max_tiles, stream)
+  st = hip_status(L.nt == 1   ? moefp4::launch_fc_decode(a, mode, false, L.max_tiles, stream)
+                  : L.nt == 8 ? moefp4::launch_fc_gemm_a8(a, false, L.max_tiles, stream)
                   : L.a8 ? moefp4::launch_fc2_a8(a, L.nt, L.max_tiles, stream)
                              : moefp4::launch_fc2_a16(a, p->gran_k, L.nt, L.max_tiles, stream),
                   "fc2");

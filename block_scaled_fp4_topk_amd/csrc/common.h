@@ -106,6 +106,23 @@ __device__ __forceinline__ int ceil_log2_over_448(float a) {
   return E - 8 + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0);
 }
 
+// E4M3 (fn) round-to-nearest-even encode of |y| <= 448, sign kept: normals
+// (|y| >= 2**-6) round the 23-bit mantissa to 3 bits, subnormals round to a
+// multiple of 2**-9.
+__device__ __forceinline__ uint32_t f32_to_e4m3_rne(float y) {
+  const uint32_t u = f2u(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t ua = u & 0x7FFFFFFFu;
+  uint32_t code;
+  if (ua >= 0x3C800000u) {
+    const uint32_t r = ua + 0x7FFFFu + ((ua >> 20) & 1u);
+    code = (r >> 20) - (120u << 3);
+  } else {
+    code = (uint32_t)__builtin_rintf(u2f(ua) * 512.0f);
+  }
+  return sign | code;
+}
+
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 
 }  // namespace moefp4

@@ -67,6 +67,11 @@ hipError_t launch_fc2_a8(const FcArgs& a, int nt, int max_tiles, hipStream_t s);
 // I % 64 == 0 (FC1) and H % 128 == 0 (FC2).
 hipError_t launch_fc_decode(const FcArgs& a, int mode, bool fc1, int max_tiles, hipStream_t s);
 
+// Prefill-shaped FP8 x FP4 grouped GEMMs on 128-row expert tiles (direct-
+// to-LDS pipelined, 256 weight rows per workgroup).  Needs K % 256 == 0,
+// I % 128 == 0 (FC1), H % 256 == 0 (FC2), 32-bit row offsets.
+hipError_t launch_fc_gemm_a8(const FcArgs& a, bool fc1, int max_tiles, hipStream_t s);
+
 // out[t, :] = sum_j w[t, j] * y[slot_of[t*k + j], :]  (f32, or rounded to bf16)
 hipError_t launch_combine(const float* y, const int32_t* slot_of, const float* topk_w, int T,
                           int k, int H, void* out, bool out_f32, hipStream_t s);

@@ -22,20 +22,6 @@ namespace {
 constexpr int kChunk = 256;          // K elements per loop iteration (2 MFMA K-steps)
 constexpr int kActStride = kChunk + 16;
 
-// E4M3 (fn) RNE encode of |y| <= 448, sign kept.
-__device__ __forceinline__ uint32_t f32_to_e4m3_rne(float y) {
-  const uint32_t u = f2u(y);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t ua = u & 0x7FFFFFFFu;
-  uint32_t code;
-  if (ua >= 0x3C800000u) {  // >= 2**-6: normal, round 23 -> 3 mantissa bits
-    const uint32_t r = ua + 0x7FFFFu + ((ua >> 20) & 1u);
-    code = (r >> 20) - (120u << 3);
-  } else {                  // subnormal quantum 2**-9
-    code = (uint32_t)__builtin_rintf(u2f(ua) * 512.0f);
-  }
-  return sign | code;
-}
 
 struct W4frag {
   uint4 c[2];    // MFMA step 0 / 1: 16 bytes = 32 codes each

@@ -42,20 +42,6 @@ __device__ __forceinline__ uint32_t dw(const uint4& v, int r) {
   return r == 0 ? v.x : r == 1 ? v.y : r == 2 ? v.z : v.w;
 }
 
-// E4M3 (fn) RNE encode of |y| <= 448, sign kept.
-__device__ __forceinline__ uint32_t f32_to_e4m3_rne(float y) {
-  const uint32_t u = f2u(y);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t ua = u & 0x7FFFFFFFu;
-  uint32_t code;
-  if (ua >= 0x3C800000u) {
-    const uint32_t r = ua + 0x7FFFFu + ((ua >> 20) & 1u);
-    code = (r >> 20) - (120u << 3);
-  } else {
-    code = (uint32_t)__builtin_rintf(u2f(ua) * 512.0f);
-  }
-  return sign | code;
-}
 
 template <int MODE, bool FC1>
 __global__ __launch_bounds__(256, 8) void fc_decode_kernel(FcArgs a) {

@@ -40,6 +40,10 @@ SMALL = (combos(synth.CONFIGS["tiny"])
          + combos(synth.variant(synth.CONFIGS["tiny"], T=16, E=32, k=4, H=1024, I=512, seed=21))
          + combos(synth.variant(synth.CONFIGS["tiny"], T=13, E=6, k=3, H=768, I=256, seed=22))
          + combos(synth.variant(synth.CONFIGS["tiny"], T=300, E=8, k=2, H=512, I=512, seed=23,
+                                routing="zipf"))
+         # prefill regime: several 128-row tiles per expert, ragged tails,
+         # an odd number of 256-wide K stages, several row blocks
+         + combos(synth.variant(synth.CONFIGS["tiny"], T=400, E=4, k=2, H=768, I=768, seed=24,
                                 routing="zipf")))
 
 
