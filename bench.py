@@ -102,7 +102,7 @@ def stage_kernel(cfg, ids, stage):
     A = ids.size
     active = len(np.unique(ids[ids >= 0]))
     mode = 2 if cfg.act == "fp8" else (0 if cfg.gran == 16 else 1)
-    gemm_ok = (mode == 2 and cfg.I % 128 == 0 and cfg.H % 256 == 0 and cfg.T * cfg.H < 2**31
+    gemm_ok = (mode == 2 and cfg.I % 512 == 0 and cfg.H % 512 == 0 and cfg.T * cfg.H < 2**31
                and A * cfg.I < 2**31 and cfg.I * cfg.H < 2**31)
     nt = (8 if gemm_ok else 4) if active and A / active > 16 else 1
     if nt == 8:

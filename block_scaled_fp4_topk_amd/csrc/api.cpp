@@ -89,7 +89,8 @@ moefp4_status plan(const moefp4_problem* p, Layout* L) {
   // 16-row tiles for decode-shaped routing; 128-row tiles for the FP8 x FP4
   // prefill GEMM (needs 32-bit row offsets and its row-block shapes); else
   // 64-row tiles
-  const bool gemm_ok = L->a8 && I % 128 == 0 && H % 256 == 0 && T * H < (1ull << 31) &&
+  const bool gemm_ok = L->a8 && I % 512 == 0 && H % 512 == 0 &&
+                       T * H < (1ull << 31) &&
                        A * I < (1ull << 31) && I * H < (1ull << 31);
   L->nt = avg > 16.0 ? (gemm_ok ? 8 : 4) : 1;
   L->tile_m = 16 * L->nt;

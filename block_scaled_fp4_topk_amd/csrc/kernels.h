@@ -68,8 +68,8 @@ hipError_t launch_fc2_a8(const FcArgs& a, int nt, int max_tiles, hipStream_t s);
 hipError_t launch_fc_decode(const FcArgs& a, int mode, bool fc1, int max_tiles, hipStream_t s);
 
 // Prefill-shaped FP8 x FP4 grouped GEMMs on 128-row expert tiles (direct-
-// to-LDS pipelined, 256 weight rows per workgroup).  Needs K % 256 == 0,
-// I % 128 == 0 (FC1), H % 256 == 0 (FC2), 32-bit row offsets.
+// to-LDS pipelined, 256 weight rows per workgroup).  Needs H % 512 == 0,
+// I % 512 == 0 and 32-bit row offsets.
 hipError_t launch_fc_gemm_a8(const FcArgs& a, bool fc1, int max_tiles, hipStream_t s);
 
 // out[t, :] = sum_j w[t, j] * y[slot_of[t*k + j], :]  (f32, or rounded to bf16)

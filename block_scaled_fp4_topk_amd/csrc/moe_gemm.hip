@@ -12,20 +12,22 @@
 // v_mfma_scale_f32_16x16x128_f8f6f4 (A = FP4 weights, B = FP8 activations),
 // FP32 accumulators in registers.
 //
-// Pipeline: K advances in stages of 256 (two 128-wide MFMA steps).  Both
-// operands of a stage go HBM/L2 -> LDS with direct-to-LDS 16-byte loads
-// (global_load_lds_dwordx4), double-buffered in two LDS stage buffers: the
-// loads of stage s + 1 are in flight while stage s is multiplied out of
-// LDS.  The block scales (8 bytes per row per stage) go through registers.
+// Pipeline: K advances in stages of 256 (two 128-wide MFMA steps).  Every
+// operand byte goes HBM/L2 -> LDS with direct-to-LDS loads
+// (global_load_lds), each instruction reading whole 128-byte lines: 8
+// activation rows x 128 bytes, or 8 weight rows x 128 bytes (a weight row's
+// 256 FP4 codes of the stage).  Two stage buffers: stage s + 1 is in flight
+// while stage s is multiplied.  The UE8M0 scales go to LDS once per group
+// of 4 stages (32 bytes per row), two lanes per row with 16-byte loads, also
+// double-buffered.
 //
-// LDS layouts (16-byte slots, XOR-swizzled so the MFMA operand reads hit
-// every bank once per 16 lanes):
-//   activations, per MFMA step: token t, 16-byte piece p (K 16p..16p+15)
-//     at slot 8 t + (p ^ ((t >> 1) & 7));
-//   weights, per MFMA step: row r, piece p (K 32p..32p+31) at slot
-//     4 r + (p ^ ((r >> 2) & 3)).
-// Every load instruction of a wave fills 64 consecutive slots: 8 tokens x
-// 128 bytes (full lines) or 16 weight rows x 64 contiguous bytes.
+// LDS layouts (16-byte slots, XOR-swizzled so that the 16 lanes of an MFMA
+// operand read hit distinct banks):
+//   activations, per MFMA step: token t, piece p (K 16p..16p+15) at slot
+//     8 t + (p ^ ((t >> 1) & 7));
+//   weights, per stage: row r, piece p (K 32p..32p+31, p < 4 first MFMA
+//     step) at slot 8 r + (p ^ ((r >> 1) & 7));
+//   scales, per group: row r, 16-byte half h at slot 2 r + h.
 //
 // Workgroup -> tile mapping: workgroups are dealt to the 8 XCDs round-robin,
 // so XCD x gets a contiguous range of (expert tile, row block) work items:
@@ -33,30 +35,30 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <type_traits>
+
 namespace moefp4 {
 
 namespace {
 
 constexpr int GM = 128;  // activation rows per tile
 constexpr int GN = 256;  // weight rows per tile
-constexpr int GK = 256;  // K per pipeline stage
+constexpr int GK = 256;  // K per pipeline stage (two MFMA steps)
+constexpr int GS = 4;    // stages per scale group (1024 K = 32 scale bytes per row)
 
-struct alignas(16) StageBuf {
+struct alignas(16) Stage {
   uint8_t act[2][1024 * 16];  // per MFMA step: 128 tokens x 8 pieces
-  uint8_t w[2][1024 * 16];    // per MFMA step: 256 rows x 4 pieces
-  uint2 asf[GM];              // the stage's 8 UE8M0 activation scale bytes per token
-  uint2 wsf[GN];              // the stage's 8 UE8M0 weight scale bytes per row
+  uint8_t w[2048 * 16];       // 256 rows x 8 pieces
 };
-
-__device__ __forceinline__ int byte_of(const uint2& v, int idx) {
-  const uint32_t w = idx < 4 ? v.x : v.y;
-  return (int)((w >> (8 * (idx & 3))) & 0xFFu);
-}
+struct alignas(16) Scales {
+  uint8_t w[GN * 32];  // per row: the group's 32 UE8M0 bytes
+  uint8_t a[GM * 32];  // per token
+};
 
 template <bool FC1>
 __global__ __launch_bounds__(256, 1) void fc_gemm_a8_kernel(FcArgs a, int nblk) {
-  __shared__ StageBuf sb0;
-  __shared__ StageBuf sb1;
+  __shared__ Stage st0, st1;
+  __shared__ Scales sc0, sc1;
   __shared__ int s_src[GM];
 
   // work item of this workgroup (XCD-contiguous ranges of the real items)
@@ -69,16 +71,17 @@ __global__ __launch_bounds__(256, 1) void fc_gemm_a8_kernel(FcArgs a, int nblk) 
   const int tile = v / nblk, nb = v - tile * nblk;
   const int e = a.tiles[2 * tile], m0 = a.tiles[2 * tile + 1];
   const int ne = a.counts[e], oe = a.offsets[e];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int r16 = lane & 15, q = lane >> 4;
   const int wm = wave >> 1, wn = wave & 1;
   const int K = a.K, N = a.N;
 
+  // source row of each tile row; rows past the expert's token count load
+  // the tile's first row instead (their MFMA columns are never stored)
   if (tid < GM) {
-    const int m = m0 + tid;
-    int src = -1;
-    if (m < ne) src = FC1 ? a.sorted_assign[oe + m] / a.top_k : oe + m;
-    s_src[tid] = src;
+    const int m = m0 + (m0 + tid < ne ? tid : 0);
+    s_src[tid] = FC1 ? a.sorted_assign[oe + m] / a.top_k : oe + m;
   }
   __syncthreads();
 
@@ -92,47 +95,46 @@ __global__ __launch_bounds__(256, 1) void fc_gemm_a8_kernel(FcArgs a, int nblk) 
   };
 
   // ---- load roles -------------------------------------------------------
-  // Instruction i (0..7) of wave w fills stage slots S = 512 w + 64 i + lane:
-  // MFMA step st = S >> 10, slot s = S & 1023.
+  // Operand instruction i (0..7) of wave w fills slots S = 512 w + 64 i +
+  // lane of the stage's activation array (MFMA step S >> 10) and of its
+  // weight array.  Scale instructions: weight slots 64 J + lane (rows
+  // 32 J + lane / 2, J = 2 w, 2 w + 1), activation slots 64 w + lane
+  // (tokens 32 w + lane / 2).
   const uint8_t* act = static_cast<const uint8_t*>(a.act);
   const uint8_t* wbase = a.w + (size_t)e * N * (size_t)(K >> 1);
-  int aoff[8], woff[8];
+  const uint8_t* wsbase = a.wsf + (size_t)e * N * (size_t)(K >> 5);
+  uint32_t aoff[8], woff[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int S = 512 * wave + 64 * i + lane;
     const int st = S >> 10, s = S & 1023;
-    {  // activations: token t, piece p
-      const int t = s >> 3, p = (s & 7) ^ ((t >> 1) & 7);
-      const int src = s_src[t];
-      aoff[i] = src >= 0 ? src * K + 128 * st + 16 * p : -1;
-    }
-    {  // weights: row r, piece p
-      const int r = s >> 2, p = (s & 3) ^ ((r >> 2) & 3);
-      woff[i] = wrow(r) * (K >> 1) + 64 * st + 16 * p;
-    }
+    const int t = s >> 3, p = (s & 7) ^ ((t >> 1) & 7);
+    aoff[i] = s_src[t] * K + 128 * st + 16 * p;
+    const int r = S >> 3, pw = (S & 7) ^ ((r >> 1) & 7);
+    woff[i] = wrow(r) * (K >> 1) + 16 * pw;
   }
-  // scale roles: weight row tid; activation token tid (tid < 128)
-  const uint8_t* wsf_p = a.wsf + ((size_t)e * N + wrow(tid)) * (size_t)(K >> 5);
-  const int asrc = tid < GM ? s_src[tid] : -1;
-  const uint8_t* asf_p = asrc >= 0 ? a.act_sf + (size_t)asrc * (K >> 5) : nullptr;
+  uint32_t wsoff[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) wsoff[j] = wrow(32 * (2 * wave + j) + (lane >> 1)) * (K >> 5) + 16 * (lane & 1);
+  const uint32_t asoff = s_src[32 * wave + (lane >> 1)] * (K >> 5) + 16 * (lane & 1);
+  const int nkb = K >> 5;  // scale bytes per row
 
-  auto issue = [&](StageBuf& b, int k0, uint2& ws, uint2& as) {
+  auto issue = [&](Stage& b, uint32_t k0) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int S0 = 512 * wave + 64 * i;  // wave-uniform first slot
-      uint8_t* abase = &b.act[S0 >> 10][(S0 & 1023) * 16];
-      uint8_t* wdst = &b.w[S0 >> 10][(S0 & 1023) * 16];
-      if (aoff[i] >= 0)
-        __builtin_amdgcn_global_load_lds(act + aoff[i] + k0, abase, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(wbase + woff[i] + (k0 >> 1), wdst, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(act + (aoff[i] + k0), &b.act[S0 >> 10][(S0 & 1023) * 16], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(wbase + (woff[i] + (k0 >> 1)), &b.w[S0 * 16], 16, 0, 0);
     }
-    ws = *reinterpret_cast<const uint2*>(wsf_p + (k0 >> 5));
-    as = uint2{0u, 0u};
-    if (asf_p) as = *reinterpret_cast<const uint2*>(asf_p + (k0 >> 5));
   };
-  auto put_scales = [&](StageBuf& b, const uint2& ws, const uint2& as) {
-    b.wsf[tid] = ws;
-    if (tid < GM) b.asf[tid] = as;
+  // scale group starting at K block kb0 (32 blocks); 16-byte pieces past the
+  // row's last scale byte are not loaded (K % 512 == 0 keeps pieces whole)
+  auto issue_scales = [&](Scales& g, int kb0) __attribute__((always_inline)) {
+    const bool ok = kb0 + 16 * (lane & 1) < nkb;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      if (ok) __builtin_amdgcn_global_load_lds(wsbase + (wsoff[j] + kb0), &g.w[(64 * (2 * wave + j)) * 16], 16, 0, 0);
+    if (ok) __builtin_amdgcn_global_load_lds(a.act_sf + (asoff + kb0), &g.a[(64 * wave) * 16], 16, 0, 0);
   };
 
   // ---- MFMA over one stage ------------------------------------------------
@@ -145,65 +147,89 @@ __global__ __launch_bounds__(256, 1) void fc_gemm_a8_kernel(FcArgs a, int nblk) 
   int ntg = (ne - m0 - 64 * wm + 15) >> 4;
   ntg = ntg < 0 ? 0 : (ntg > 4 ? 4 : ntg);
 
-  auto compute = [&](const StageBuf& b) {
+  // stage b with scale group g, stage index gs within the group; FULL: all 4
+  // token groups (straight-line code), else the first ntg
+  auto compute_t = [&](const Stage& b, const Scales& g, int gs, auto full) __attribute__((always_inline)) {
+    constexpr bool FULL = decltype(full)::value;
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      v8i A[8];
-      int sa[8];
+    for (int ms = 0; ms < 2; ++ms) {
+      const int kb = 8 * gs + 4 * ms + q;  // this lane's K block within the group
+      v8i B[4];
+      int sb[4];
+#pragma unroll
+      for (int tg = 0; tg < 4; ++tg) {
+        if (FULL || tg < ntg) {
+          const int t = 64 * wm + 16 * tg + r16;
+          const int x = (t >> 1) & 7;
+          const uint4 b0 = *reinterpret_cast<const uint4*>(&b.act[ms][(8 * t + (q ^ x)) * 16]);
+          const uint4 b1 = *reinterpret_cast<const uint4*>(&b.act[ms][(8 * t + ((q + 4) ^ x)) * 16]);
+          B[tg] = v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w,
+                      (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+          sb[tg] = g.a[t * 32 + kb];
+        }
+      }
 #pragma unroll
       for (int rg = 0; rg < 8; ++rg) {
         const int r = FC1 ? (rg < 4 ? 64 * wn + 16 * rg : 128 + 64 * wn + 16 * (rg - 4)) + r16
                           : 128 * wn + 16 * rg + r16;
         const uint4 c = *reinterpret_cast<const uint4*>(
-            &b.w[st][(4 * r + (q ^ ((r >> 2) & 3))) * 16]);
-        A[rg] = v8i{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
-        sa[rg] = byte_of(b.wsf[r], 4 * st + q);
-      }
+            &b.w[(8 * r + ((4 * ms + q) ^ ((r >> 1) & 7))) * 16]);
+        const v8i A = {(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
+        const int sa = g.w[r * 32 + kb];
 #pragma unroll
-      for (int tg = 0; tg < 4; ++tg) {
-        if (tg < ntg) {
-          const int t = 64 * wm + 16 * tg + r16;
-          const int x = (t >> 1) & 7;
-          const uint4 b0 = *reinterpret_cast<const uint4*>(&b.act[st][(8 * t + (q ^ x)) * 16]);
-          const uint4 b1 = *reinterpret_cast<const uint4*>(&b.act[st][(8 * t + ((q + 4) ^ x)) * 16]);
-          const v8i B = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w,
-                         (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
-          const int sb = byte_of(b.asf[t], 4 * st + q);
-#pragma unroll
-          for (int rg = 0; rg < 8; ++rg)
-            acc[rg][tg] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[rg], B, acc[rg][tg], 4, 0,
-                                                                          0, sa[rg], 0, sb);
-        }
+        for (int tg = 0; tg < 4; ++tg)
+          if (FULL || tg < ntg)
+            acc[rg][tg] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B[tg], acc[rg][tg], 4, 0,
+                                                                          0, sa, 0, sb[tg]);
       }
     }
   };
+  auto compute = [&](const Stage& b, const Scales& g, int gs) __attribute__((always_inline)) {
+    if (ntg == 4) compute_t(b, g, gs, std::true_type{});
+    else compute_t(b, g, gs, std::false_type{});
+  };
 
-  // ---- pipeline ---------------------------------------------------------
-  // vmcnt(0) (expcnt and lgkmcnt left at their maxima): the direct-to-LDS
-  // loads of the next stage have landed
-  constexpr int kWaitVm0 = 0x0F70;
+  // ---- pipeline -----------------------------------------------------------
+  // Step c: wait until this wave's loads (stage c, and the scale group of
+  // stage c when it starts one) have landed, barrier (every wave's loads
+  // visible, every wave done with stage c - 1), start loading stage c + 1
+  // into the other stage buffer (and, at a group start, the next scale
+  // group into the other scale buffer), multiply stage c.  Buffers are
+  // compile-time choices (unrolled by 2 groups = 8 stages) so the compiler
+  // sees that loads in flight never alias the buffers being read.
+  auto barrier = [&]() __attribute__((always_inline)) {
+    // plain s_barrier (__syncthreads() would also wait for the loads just
+    // issued); the asm statements keep LDS accesses on their side
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
   const int ns = K / GK;
-  uint2 ws, as;
-  issue(sb0, 0, ws, as);
-  __builtin_amdgcn_s_waitcnt(kWaitVm0);
-  put_scales(sb0, ws, as);
-  __syncthreads();
-  for (int c = 0; c < ns; c += 2) {
-    if (c + 1 < ns) issue(sb1, (c + 1) * GK, ws, as);
-    compute(sb0);
-    if (c + 1 < ns) {
-      __builtin_amdgcn_s_waitcnt(kWaitVm0);
-      put_scales(sb1, ws, as);
-    }
-    __syncthreads();
+  auto step = [&](Stage& cur, Stage& nxt, Scales& g, Scales& gnext, int c) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    barrier();
+    if (c + 1 < ns) issue(nxt, (c + 1) * GK);
+    if ((c & (GS - 1)) == 0 && c + GS < ns) issue_scales(gnext, (c + GS) * (GK / 32));
+    compute(cur, g, c & (GS - 1));
+  };
+  issue_scales(sc0, 0);
+  issue(st0, 0);
+  for (int c = 0; c < ns; c += 2 * GS) {
+    step(st0, st1, sc0, sc1, c);
     if (c + 1 >= ns) break;
-    if (c + 2 < ns) issue(sb0, (c + 2) * GK, ws, as);
-    compute(sb1);
-    if (c + 2 < ns) {
-      __builtin_amdgcn_s_waitcnt(kWaitVm0);
-      put_scales(sb0, ws, as);
-    }
-    __syncthreads();
+    step(st1, st0, sc0, sc1, c + 1);
+    if (c + 2 >= ns) break;
+    step(st0, st1, sc0, sc1, c + 2);
+    if (c + 3 >= ns) break;
+    step(st1, st0, sc0, sc1, c + 3);
+    if (c + 4 >= ns) break;
+    step(st0, st1, sc1, sc0, c + 4);
+    if (c + 5 >= ns) break;
+    step(st1, st0, sc1, sc0, c + 5);
+    if (c + 6 >= ns) break;
+    step(st0, st1, sc1, sc0, c + 6);
+    if (c + 7 >= ns) break;
+    step(st1, st0, sc1, sc0, c + 7);
   }
 
   // ---- epilogue ---------------------------------------------------------

@@ -42,8 +42,9 @@ SMALL = (combos(synth.CONFIGS["tiny"])
          + combos(synth.variant(synth.CONFIGS["tiny"], T=300, E=8, k=2, H=512, I=512, seed=23,
                                 routing="zipf"))
          # prefill regime: several 128-row tiles per expert, ragged tails,
-         # an odd number of 256-wide K stages, several row blocks
-         + combos(synth.variant(synth.CONFIGS["tiny"], T=400, E=4, k=2, H=768, I=768, seed=24,
+         # several row blocks, K = 1536 (a partial last scale group) and
+         # K = 1024 (one whole group)
+         + combos(synth.variant(synth.CONFIGS["tiny"], T=400, E=4, k=2, H=1536, I=1024, seed=24,
                                 routing="zipf")))
 
 
