@@ -41,7 +41,8 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
   size_t flags, counts, offsets, sorted, slot_of, tiles, ntiles;
-  size_t act_scale, x16, hmax, h, h_sf, y, total;
+  size_t act_scale, x16, hmax, h, h_sf, y, route_hist, total;
+  int route_chunks, route_chunk;
   int tile_m, nt, max_tiles;
   bool a8, g16_a16;
 };
@@ -110,6 +111,13 @@ moefp4_status plan(const moefp4_problem* p, Layout* L) {
   L->h = take(L->a8 ? A * I : A * I * 2);
   L->h_sf = take(L->a8 ? A * (I / 32) : 0);
   L->y = take(A * H * 4);
+  L->route_chunks = 0;
+  L->route_chunk = 0;
+  if ((long long)A > moefp4::kRouteSingleMax) {
+    L->route_chunk = moefp4::route_chunk((long long)A);
+    L->route_chunks = (int)((A + L->route_chunk - 1) / L->route_chunk);
+  }
+  L->route_hist = take((size_t)L->route_chunks * (E + 1) * 4);
   L->total = o;
   return MOEFP4_OK;
 }
@@ -144,6 +152,9 @@ moefp4_status route_into(const moefp4_problem* p, const Layout& L, const int32_t
   o.T = p->T;
   o.H = p->H;
   o.row_scale = row_scale;
+  o.nchunks = L.route_chunks;
+  o.chunk = L.route_chunk;
+  o.hist = L.route_chunks ? at<int32_t>(ws, L.route_hist) : nullptr;
   return hip_status(moefp4::launch_route(ids, p->T * p->top_k, p->E, L.tile_m, o, s), "route");
 }
 

@@ -27,7 +27,20 @@ struct RouteOut {
   const uint16_t* x;
   int T, H;
   float* row_scale;
+  // multi-workgroup form (nchunks > 0): chunks of `chunk` assignments and a
+  // [nchunks][E + 1] int32 scratch for their histograms / starts
+  int nchunks, chunk;
+  int32_t* hist;
 };
+
+// Assignments per chunk of the multi-workgroup route (T * k above
+// kRouteSingleMax uses it).
+constexpr int kRouteSingleMax = 8192;
+inline int route_chunk(long long A) {
+  long long c = (A + 63) / 64;
+  c = (c + 1023) / 1024 * 1024;
+  return (int)(c < 4096 ? 4096 : c);
+}
 
 hipError_t launch_route(const int32_t* topk_ids, int A, int E, int tile_m, const RouteOut& o,
                         hipStream_t s);

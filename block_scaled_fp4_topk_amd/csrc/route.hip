@@ -56,9 +56,10 @@ __device__ __forceinline__ int row_exponent(uint32_t maxbits) {
 }
 
 // One wavefront per row: the row's largest |x| (compared as bit patterns).
-__device__ void row_scales(const RouteOut& o) {
+// Workgroup b of nb workgroups takes rows 16 b + wave, 16 (b + nb) + wave, ...
+__device__ void row_scales_from(const RouteOut& o, int b, int nb) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int t = (blockIdx.x - 1) * kRouteWaves + wave; t < o.T; t += (gridDim.x - 1) * kRouteWaves) {
+  for (int t = b * kRouteWaves + wave; t < o.T; t += nb * kRouteWaves) {
     const uint16_t* row = o.x + (size_t)t * o.H;
     uint32_t m = 0;
     for (int i = lane * 8; i < o.H; i += 512) {
@@ -79,6 +80,78 @@ __device__ void row_scales(const RouteOut& o) {
   }
 }
 
+// Stable scatter of assignments [a0, a1), 1024 per pass, to s_base[e] +
+// (rank among earlier assignments of expert e); s_base advances per pass.
+// Within a wavefront the rank comes from ballots over the bits of the expert
+// id, across wavefronts from per-wave counts in LDS.
+__device__ void scatter_range(const int32_t* __restrict__ ids, int a0, int a1, int E, int* s_base,
+                              int* s_wc, const RouteOut& o) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  for (int c0 = a0; c0 < a1; c0 += kRouteThreads) {
+    for (int i = tid; i < kRouteWaves * E; i += kRouteThreads) s_wc[i] = 0;
+    const int a = c0 + tid;
+    const int e = a < a1 ? ids[a] : -1;
+    const bool valid = a < a1 && (unsigned)e < (unsigned)E;
+    uint64_t peers = ballot(valid);
+    const int key = valid ? e : 0;
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (key >> b) & 1;
+      const uint64_t m = ballot(bit);
+      peers &= bit ? m : ~m;
+    }
+    const int rank = __popcll(peers & ((1ull << lane) - 1ull));
+    __syncthreads();  // s_wc cleared
+    if (valid && rank == 0) s_wc[wave * E + e] = __popcll(peers);
+    __syncthreads();
+    if (valid) {
+      int pos = s_base[e] + rank;
+      for (int w = 0; w < wave; ++w) pos += s_wc[w * E + e];
+      o.sorted_assign[pos] = a;
+      o.slot_of[a] = pos;
+    } else if (a < a1) {
+      o.slot_of[a] = -1;
+    }
+    __syncthreads();
+    for (int ee = tid; ee < E; ee += kRouteThreads) {
+      int s = 0;
+      for (int w = 0; w < kRouteWaves; ++w) s += s_wc[w * E + ee];
+      s_base[ee] += s;
+    }
+    __syncthreads();
+  }
+}
+
+// Counts and scans shared by both forms: expert counts c (thread e), their
+// exclusive offsets, the tile list, the dropped count.  Returns the number
+// of valid assignments.
+__device__ int finish_counts(int c, int E, int tile_m, int drops, int* s_tmp, int* s_base,
+                             const RouteOut& o) {
+  const int tid = threadIdx.x;
+  int valid_total;
+  const int base = block_exclusive_scan(c, s_tmp, &valid_total);
+  const int nt = (c + tile_m - 1) / tile_m;
+  int tiles_total;
+  const int tbase = block_exclusive_scan(nt, s_tmp, &tiles_total);
+  if (tid < E) {
+    o.counts[tid] = c;
+    o.offsets[tid] = base;
+    s_base[tid] = base;
+    for (int i = 0; i < nt; ++i) {
+      o.tiles[2 * (tbase + i)] = tid;
+      o.tiles[2 * (tbase + i) + 1] = i * tile_m;
+    }
+  }
+  if (tid == 0) {
+    o.offsets[E] = valid_total;
+    o.ntiles[0] = tiles_total;
+    o.flags[0] = drops;
+  }
+  return valid_total;
+}
+
+// Single-workgroup route (small T * k): histogram, scans, stable scatter.
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t* __restrict__ ids,
                                                               int A, int E, int tile_m,
                                                               RouteOut o) {
@@ -91,7 +164,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t* __r
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // workgroups past the first compute the per-row staging scales instead
   if (blockIdx.x > 0) {
-    row_scales(o);
+    row_scales_from(o, blockIdx.x - 1, gridDim.x - 1);
     return;
   }
 
@@ -111,63 +184,79 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t* __r
   __syncthreads();
 
   // 2. exclusive scans: expert offsets and tile offsets (E <= 1024 = threads)
-  const int c = tid < E ? s_cnt[tid] : 0;
-  int valid_total;
-  const int base = block_exclusive_scan(c, s_tmp, &valid_total);
-  const int nt = (c + tile_m - 1) / tile_m;
-  int tiles_total;
-  const int tbase = block_exclusive_scan(nt, s_tmp, &tiles_total);
-  if (tid < E) {
-    o.counts[tid] = c;
-    o.offsets[tid] = base;
-    s_base[tid] = base;
-    for (int i = 0; i < nt; ++i) {
-      o.tiles[2 * (tbase + i)] = tid;
-      o.tiles[2 * (tbase + i) + 1] = i * tile_m;
-    }
-  }
-  if (tid == 0) {
-    o.offsets[E] = valid_total;
-    o.ntiles[0] = tiles_total;
-    o.flags[0] = s_drop;
-  }
+  const int valid_total = finish_counts(tid < E ? s_cnt[tid] : 0, E, tile_m, s_drop, s_tmp, s_base, o);
+  // 3. stable scatter
+  scatter_range(ids, 0, A, E, s_base, s_wc, o);
+  for (int i = valid_total + tid; i < A; i += kRouteThreads) o.sorted_assign[i] = -1;
+}
 
-  // 3. stable scatter, 1024 assignments per pass
-  int nbits = 0;
-  while ((1 << nbits) < E) ++nbits;
-  for (int c0 = 0; c0 < A; c0 += kRouteThreads) {
-    for (int i = tid; i < kRouteWaves * E; i += kRouteThreads) s_wc[i] = 0;
-    const int a = c0 + tid;
-    const int e = a < A ? ids[a] : -1;
-    const bool valid = a < A && (unsigned)e < (unsigned)E;
-    uint64_t peers = ballot(valid);
-    const int key = valid ? e : 0;
-    for (int b = 0; b < nbits; ++b) {
-      const bool bit = (key >> b) & 1;
-      const uint64_t m = ballot(bit);
-      peers &= bit ? m : ~m;
+// Multi-workgroup route (large T * k), three launches over chunks of
+// o.chunk assignments: per-chunk histograms, one workgroup that scans them
+// (chunk g of expert e starts at offsets[e] + the counts of e in chunks
+// before g), and per-chunk stable scatters.  Same result as the single
+// workgroup form.
+__global__ __launch_bounds__(kRouteThreads) void route_hist_kernel(const int32_t* __restrict__ ids,
+                                                                   int A, int E, RouteOut o) {
+  __shared__ int s_cnt[kMaxExperts];
+  __shared__ int s_drop;
+  const int tid = threadIdx.x;
+  if (blockIdx.x >= o.nchunks) {
+    row_scales_from(o, blockIdx.x - o.nchunks, gridDim.x - o.nchunks);
+    return;
+  }
+  for (int e = tid; e < E; e += kRouteThreads) s_cnt[e] = 0;
+  if (tid == 0) s_drop = 0;
+  __syncthreads();
+  const int a0 = blockIdx.x * o.chunk, a1 = min(A, a0 + o.chunk);
+  int drop = 0;
+  for (int a = a0 + tid; a < a1; a += kRouteThreads) {
+    const int e = ids[a];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&s_cnt[e], 1);
+    else ++drop;
+  }
+  if (drop) atomicAdd(&s_drop, drop);
+  __syncthreads();
+  int32_t* h = o.hist + (size_t)blockIdx.x * (E + 1);
+  for (int e = tid; e < E; e += kRouteThreads) h[e] = s_cnt[e];
+  if (tid == 0) h[E] = s_drop;
+}
+
+__global__ __launch_bounds__(kRouteThreads) void route_scan_kernel(int A, int E, int tile_m,
+                                                                   RouteOut o) {
+  __shared__ int s_base[kMaxExperts];
+  __shared__ int s_tmp[128];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < o.n_zero; i += kRouteThreads) o.zero_words[i] = 0u;
+  int c = 0, drops = 0;
+  if (tid < E)
+    for (int g = 0; g < o.nchunks; ++g) c += o.hist[(size_t)g * (E + 1) + tid];
+  if (tid == 0)
+    for (int g = 0; g < o.nchunks; ++g) drops += o.hist[(size_t)g * (E + 1) + E];
+  const int valid_total = finish_counts(c, E, tile_m, drops, s_tmp, s_base, o);
+  __syncthreads();
+  // per-chunk starts, in place
+  if (tid < E) {
+    int run = s_base[tid];
+    for (int g = 0; g < o.nchunks; ++g) {
+      int32_t* h = o.hist + (size_t)g * (E + 1) + tid;
+      const int n = *h;
+      *h = run;
+      run += n;
     }
-    const int rank = __popcll(peers & ((1ull << lane) - 1ull));
-    __syncthreads();  // s_wc cleared
-    if (valid && rank == 0) s_wc[wave * E + e] = __popcll(peers);
-    __syncthreads();
-    if (valid) {
-      int pos = s_base[e] + rank;
-      for (int w = 0; w < wave; ++w) pos += s_wc[w * E + e];
-      o.sorted_assign[pos] = a;
-      o.slot_of[a] = pos;
-    } else if (a < A) {
-      o.slot_of[a] = -1;
-    }
-    __syncthreads();
-    for (int ee = tid; ee < E; ee += kRouteThreads) {
-      int s = 0;
-      for (int w = 0; w < kRouteWaves; ++w) s += s_wc[w * E + ee];
-      s_base[ee] += s;
-    }
-    __syncthreads();
   }
   for (int i = valid_total + tid; i < A; i += kRouteThreads) o.sorted_assign[i] = -1;
+}
+
+__global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(const int32_t* __restrict__ ids,
+                                                                      int A, int E, RouteOut o) {
+  extern __shared__ int smem[];
+  int* s_base = smem;       // [E]
+  int* s_wc = s_base + E;   // [kRouteWaves][E]
+  const int g = blockIdx.x;
+  for (int e = threadIdx.x; e < E; e += kRouteThreads) s_base[e] = o.hist[(size_t)g * (E + 1) + e];
+  __syncthreads();
+  const int a0 = g * o.chunk, a1 = min(A, a0 + o.chunk);
+  scatter_range(ids, a0, a1, E, s_base, s_wc, o);
 }
 
 __global__ __launch_bounds__(256) void rows_to_f16_kernel(const uint16_t* __restrict__ x, int T,
@@ -210,8 +299,20 @@ hipError_t launch_route(const int32_t* topk_ids, int A, int E, int tile_m, const
     scale_blocks = (o.T + kRouteWaves - 1) / kRouteWaves;
     scale_blocks = scale_blocks > 256 ? 256 : scale_blocks;
   }
-  hipLaunchKernelGGL(route_kernel, dim3(1 + scale_blocks), dim3(kRouteThreads), lds, s, topk_ids, A,
-                     E, tile_m, o);
+  if (o.nchunks <= 0) {
+    hipLaunchKernelGGL(route_kernel, dim3(1 + scale_blocks), dim3(kRouteThreads), lds, s, topk_ids, A,
+                       E, tile_m, o);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(route_hist_kernel, dim3(o.nchunks + scale_blocks), dim3(kRouteThreads), 0, s,
+                     topk_ids, A, E, o);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(kRouteThreads), 0, s, A, E, tile_m, o);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(route_scatter_kernel, dim3(o.nchunks), dim3(kRouteThreads), lds, s, topk_ids, A,
+                     E, o);
   return hipGetLastError();
 }
 

@@ -21,6 +21,10 @@ CASES = [
     ("e512", 100, 512, 4, "softmax_topk", False),
     ("single", 1, 1, 1, "softmax_topk", False),
     ("invalid_ids", 300, 16, 4, "softmax_topk", True),
+    # more than 8192 assignments: the multi-workgroup form (chunks of 4096,
+    # a ragged last chunk)
+    ("multi_invalid", 3000, 64, 4, "softmax_topk", True),
+    ("multi_e512", 2100, 512, 8, "zipf", False),
 ]
 
 
