@@ -12,22 +12,20 @@
 // v_mfma_scale_f32_16x16x128_f8f6f4 (A = FP4 weights, B = FP8 activations),
 // FP32 accumulators in registers.
 //
-// Pipeline: K advances in stages of 256 (two 128-wide MFMA steps).  Every
-// operand byte goes HBM/L2 -> LDS with direct-to-LDS loads
-// (global_load_lds), each instruction reading whole 128-byte lines: 8
-// activation rows x 128 bytes, or 8 weight rows x 128 bytes (a weight row's
-// 256 FP4 codes of the stage).  Two stage buffers: stage s + 1 is in flight
-// while stage s is multiplied.  The UE8M0 scales go to LDS once per group
-// of 4 stages (32 bytes per row), two lanes per row with 16-byte loads, also
-// double-buffered.
+// Pipeline: K advances in stages of 128 (one MFMA step).  Both operands of
+// a stage go HBM/L2 -> LDS with direct-to-LDS 16-byte loads
+// (global_load_lds_dwordx4): 8 activation rows x 128 bytes or 16 weight rows
+// x 64 bytes per instruction.  A ring of 4 stage buffers keeps the loads of
+// three stages in flight while one is multiplied; the UE8M0 block scales of
+// a group of 4 stages (16 bytes per row or token) go straight to registers,
+// one group ahead.  A wave whose 64 activation rows hold no token skips its
+// MFMAs.
 //
 // LDS layouts (16-byte slots, XOR-swizzled so that the 16 lanes of an MFMA
 // operand read hit distinct banks):
-//   activations, per MFMA step: token t, piece p (K 16p..16p+15) at slot
+//   activations: token t, piece p (K 16p..16p+15) at slot
 //     8 t + (p ^ ((t >> 1) & 7));
-//   weights, per stage: row r, piece p (K 32p..32p+31, p < 4 first MFMA
-//     step) at slot 8 r + (p ^ ((r >> 1) & 7));
-//   scales, per group: row r, 16-byte half h at slot 2 r + h.
+//   weights: row r, piece p (K 32p..32p+31) at slot 4 r + (p ^ ((r >> 2) & 3)).
 //
 // Workgroup -> tile mapping: workgroups are dealt to the 8 XCDs round-robin,
 // so XCD x gets a contiguous range of (expert tile, row block) work items:
@@ -43,22 +41,21 @@ namespace {
 
 constexpr int GM = 128;  // activation rows per tile
 constexpr int GN = 256;  // weight rows per tile
-constexpr int GK = 256;  // K per pipeline stage (two MFMA steps)
-constexpr int GS = 4;    // stages per scale group (1024 K = 32 scale bytes per row)
+constexpr int GK = 128;  // K per pipeline stage (one MFMA step)
+constexpr int GS = 4;    // stages per scale group (512 K = 16 scale bytes per row)
 
 struct alignas(16) Stage {
-  uint8_t act[2][1024 * 16];  // per MFMA step: 128 tokens x 8 pieces
-  uint8_t w[2048 * 16];       // 256 rows x 8 pieces
+  uint8_t act[1024 * 16];  // 128 tokens x 8 pieces
+  uint8_t w[1024 * 16];    // 256 rows x 4 pieces
 };
-struct alignas(16) Scales {
-  uint8_t w[GN * 32];  // per row: the group's 32 UE8M0 bytes
-  uint8_t a[GM * 32];  // per token
-};
+// s_waitcnt with vmcnt(n), expcnt and lgkmcnt at their maxima (gfx9 encoding)
+#define WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x0F70)
+constexpr int kOps = 8;       // operand load instructions per wave per stage
+constexpr int kScaleOps = 12;  // scale load instructions per wave per group (8 weight, 4 activation)
 
 template <bool FC1>
 __global__ __launch_bounds__(256, 1) void fc_gemm_a8_kernel(FcArgs a, int nblk) {
-  __shared__ Stage st0, st1;
-  __shared__ Scales sc0, sc1;
+  __shared__ Stage st0, st1, st2, st3;
   __shared__ int s_src[GM];
 
   // work item of this workgroup (XCD-contiguous ranges of the real items)
@@ -95,46 +92,28 @@ __global__ __launch_bounds__(256, 1) void fc_gemm_a8_kernel(FcArgs a, int nblk) 
   };
 
   // ---- load roles -------------------------------------------------------
-  // Operand instruction i (0..7) of wave w fills slots S = 512 w + 64 i +
-  // lane of the stage's activation array (MFMA step S >> 10) and of its
-  // weight array.  Scale instructions: weight slots 64 J + lane (rows
-  // 32 J + lane / 2, J = 2 w, 2 w + 1), activation slots 64 w + lane
-  // (tokens 32 w + lane / 2).
+  // Operand instruction i (0..3) of wave w fills slots S = 256 w + 64 i +
+  // lane of the stage's activation and weight arrays.
   const uint8_t* act = static_cast<const uint8_t*>(a.act);
   const uint8_t* wbase = a.w + (size_t)e * N * (size_t)(K >> 1);
   const uint8_t* wsbase = a.wsf + (size_t)e * N * (size_t)(K >> 5);
-  uint32_t aoff[8], woff[8];
+  uint32_t aoff[4], woff[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int S = 512 * wave + 64 * i + lane;
-    const int st = S >> 10, s = S & 1023;
-    const int t = s >> 3, p = (s & 7) ^ ((t >> 1) & 7);
-    aoff[i] = s_src[t] * K + 128 * st + 16 * p;
-    const int r = S >> 3, pw = (S & 7) ^ ((r >> 1) & 7);
+  for (int i = 0; i < 4; ++i) {
+    const int S = 256 * wave + 64 * i + lane;
+    const int t = S >> 3, p = (S & 7) ^ ((t >> 1) & 7);
+    aoff[i] = s_src[t] * K + 16 * p;
+    const int r = S >> 2, pw = (S & 3) ^ ((r >> 2) & 3);
     woff[i] = wrow(r) * (K >> 1) + 16 * pw;
   }
-  uint32_t wsoff[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) wsoff[j] = wrow(32 * (2 * wave + j) + (lane >> 1)) * (K >> 5) + 16 * (lane & 1);
-  const uint32_t asoff = s_src[32 * wave + (lane >> 1)] * (K >> 5) + 16 * (lane & 1);
-  const int nkb = K >> 5;  // scale bytes per row
-
+  // (uniform 64-bit base + 32-bit lane offset: the scalar-base address form)
   auto issue = [&](Stage& b, uint32_t k0) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int S0 = 512 * wave + 64 * i;  // wave-uniform first slot
-      __builtin_amdgcn_global_load_lds(act + (aoff[i] + k0), &b.act[S0 >> 10][(S0 & 1023) * 16], 16, 0, 0);
+    for (int i = 0; i < 4; ++i) {
+      const int S0 = 256 * wave + 64 * i;  // wave-uniform first slot
+      __builtin_amdgcn_global_load_lds(act + (aoff[i] + k0), &b.act[S0 * 16], 16, 0, 0);
       __builtin_amdgcn_global_load_lds(wbase + (woff[i] + (k0 >> 1)), &b.w[S0 * 16], 16, 0, 0);
     }
-  };
-  // scale group starting at K block kb0 (32 blocks); 16-byte pieces past the
-  // row's last scale byte are not loaded (K % 512 == 0 keeps pieces whole)
-  auto issue_scales = [&](Scales& g, int kb0) __attribute__((always_inline)) {
-    const bool ok = kb0 + 16 * (lane & 1) < nkb;
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-      if (ok) __builtin_amdgcn_global_load_lds(wsbase + (wsoff[j] + kb0), &g.w[(64 * (2 * wave + j)) * 16], 16, 0, 0);
-    if (ok) __builtin_amdgcn_global_load_lds(a.act_sf + (asoff + kb0), &g.a[(64 * wave) * 16], 16, 0, 0);
   };
 
   // ---- MFMA over one stage ------------------------------------------------
@@ -143,93 +122,142 @@ __global__ __launch_bounds__(256, 1) void fc_gemm_a8_kernel(FcArgs a, int nblk) 
   for (int rg = 0; rg < 8; ++rg)
 #pragma unroll
     for (int tg = 0; tg < 4; ++tg) acc[rg][tg] = v4f{0.f, 0.f, 0.f, 0.f};
-  // token groups of this wave that hold at least one token
-  int ntg = (ne - m0 - 64 * wm + 15) >> 4;
-  ntg = ntg < 0 ? 0 : (ntg > 4 ? 4 : ntg);
+  // a wave whose 64 tile rows hold no token skips its MFMAs; otherwise all
+  // four 16-row groups are multiplied (rows past the token count are
+  // never stored)
+  const bool wave_has_tokens = ne - m0 - 64 * wm > 0;
 
-  // stage b with scale group g, stage index gs within the group; FULL: all 4
-  // token groups (straight-line code), else the first ntg
-  auto compute_t = [&](const Stage& b, const Scales& g, int gs, auto full) __attribute__((always_inline)) {
-    constexpr bool FULL = decltype(full)::value;
+  // Per-lane LDS offsets (bytes): the swizzle terms depend only on the lane
+  // (row and token group bases are multiples of 16), so every operand read
+  // of a stage is one of these plus a compile-time or wave-uniform offset.
+  const int lw = 16 * (4 * r16 + (q ^ ((r16 >> 2) & 3)));     // weight row r16, piece q
+  const int xr = (r16 >> 1) & 7;
+  const int la0 = 16 * (8 * r16 + (q ^ xr));                  // token r16, piece q
+  const int la1 = 16 * (8 * r16 + ((q + 4) ^ xr));            // token r16, piece q + 4
+  // first WG-local weight row of row group rg
+  auto rbase = [&](int rg) { return FC1 ? (rg < 4 ? 64 * wn + 16 * rg : 128 + 64 * wn + 16 * (rg - 4))
+                                        : 128 * wn + 16 * rg; };
+
+  // UE8M0 scales, in registers: per group of 4 stages (16 K blocks) the lane
+  // holds the 16 scale bytes of its row in each row group and of its token
+  // in each token group; stage gs of the group uses byte 4 gs + q.
+  struct GroupScales { uint4 w[8], a[4]; };
+  const uint8_t* wsrow[8];
 #pragma unroll
-    for (int ms = 0; ms < 2; ++ms) {
-      const int kb = 8 * gs + 4 * ms + q;  // this lane's K block within the group
-      v8i B[4];
-      int sb[4];
+  for (int rg = 0; rg < 8; ++rg) wsrow[rg] = wsbase + (size_t)wrow(rbase(rg) + r16) * (K >> 5);
+  const uint8_t* asrow[4];
 #pragma unroll
-      for (int tg = 0; tg < 4; ++tg) {
-        if (FULL || tg < ntg) {
-          const int t = 64 * wm + 16 * tg + r16;
-          const int x = (t >> 1) & 7;
-          const uint4 b0 = *reinterpret_cast<const uint4*>(&b.act[ms][(8 * t + (q ^ x)) * 16]);
-          const uint4 b1 = *reinterpret_cast<const uint4*>(&b.act[ms][(8 * t + ((q + 4) ^ x)) * 16]);
-          B[tg] = v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w,
-                      (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
-          sb[tg] = g.a[t * 32 + kb];
-        }
-      }
+  for (int tg = 0; tg < 4; ++tg) asrow[tg] = a.act_sf + (size_t)s_src[64 * wm + 16 * tg + r16] * (K >> 5);
+  auto load_scales = [&](GroupScales& g, int kb0) __attribute__((always_inline)) {
 #pragma unroll
-      for (int rg = 0; rg < 8; ++rg) {
-        const int r = FC1 ? (rg < 4 ? 64 * wn + 16 * rg : 128 + 64 * wn + 16 * (rg - 4)) + r16
-                          : 128 * wn + 16 * rg + r16;
-        const uint4 c = *reinterpret_cast<const uint4*>(
-            &b.w[(8 * r + ((4 * ms + q) ^ ((r >> 1) & 7))) * 16]);
-        const v8i A = {(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
-        const int sa = g.w[r * 32 + kb];
+    for (int rg = 0; rg < 8; ++rg) g.w[rg] = *reinterpret_cast<const uint4*>(wsrow[rg] + kb0);
 #pragma unroll
-        for (int tg = 0; tg < 4; ++tg)
-          if (FULL || tg < ntg)
-            acc[rg][tg] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B[tg], acc[rg][tg], 4, 0,
-                                                                          0, sa, 0, sb[tg]);
-      }
+    for (int tg = 0; tg < 4; ++tg) g.a[tg] = *reinterpret_cast<const uint4*>(asrow[tg] + kb0);
+  };
+  auto sbyte = [&](const uint4& v, int gs) {
+    const uint32_t w = gs == 0 ? v.x : gs == 1 ? v.y : gs == 2 ? v.z : v.w;
+    return (int)((w >> (8 * q)) & 0xFFu);
+  };
+
+  // stage b with scale group g, stage index gs within the group
+  auto compute = [&](const Stage& b, const GroupScales& g, int gs) __attribute__((always_inline)) {
+    if (!wave_has_tokens) return;
+    v8i A[8];
+#pragma unroll
+    for (int rg = 0; rg < 8; ++rg) {
+      const uint4 c = *reinterpret_cast<const uint4*>(&b.w[64 * rbase(rg) + lw]);
+      A[rg] = v8i{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int tg = 0; tg < 4; ++tg) {
+      const int tb = 64 * wm + 16 * tg;
+      const uint4 b0 = *reinterpret_cast<const uint4*>(&b.act[128 * tb + la0]);
+      const uint4 b1 = *reinterpret_cast<const uint4*>(&b.act[128 * tb + la1]);
+      const v8i B = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w,
+                     (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+      const int sb = sbyte(g.a[tg], gs);
+#pragma unroll
+      for (int rg = 0; rg < 8; ++rg)
+        acc[rg][tg] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[rg], B, acc[rg][tg], 4, 0, 0,
+                                                                      sbyte(g.w[rg], gs), 0, sb);
     }
   };
-  auto compute = [&](const Stage& b, const Scales& g, int gs) __attribute__((always_inline)) {
-    if (ntg == 4) compute_t(b, g, gs, std::true_type{});
-    else compute_t(b, g, gs, std::false_type{});
-  };
 
-  // ---- pipeline -----------------------------------------------------------
-  // Step c: wait until this wave's loads (stage c, and the scale group of
-  // stage c when it starts one) have landed, barrier (every wave's loads
-  // visible, every wave done with stage c - 1), start loading stage c + 1
-  // into the other stage buffer (and, at a group start, the next scale
-  // group into the other scale buffer), multiply stage c.  Buffers are
-  // compile-time choices (unrolled by 2 groups = 8 stages) so the compiler
-  // sees that loads in flight never alias the buffers being read.
+  // ---- pipeline: 4-stage ring, loads 3 stages ahead ------------------------
+  // Stage c lives in ring buffer c % 4; the scales of group c / 4 in
+  // registers, loaded one group ahead.  Step c: wait until this wave's loads of stage c (and of
+  // its scale group) have landed -- the loads of the next two stages stay
+  // in flight --, barrier (every wave's loads visible, every wave done with
+  // stage c - 1), at a group start load the next scale group into the other
+  // scale buffer, load stage c + 3 into the buffer stage c - 1 used,
+  // multiply stage c.  Buffers are compile-time choices (the loop is
+  // unrolled by the ring size) so the compiler sees that the loads in flight
+  // never alias the buffers being read, and the vmcnt thresholds are static.
   auto barrier = [&]() __attribute__((always_inline)) {
-    // plain s_barrier (__syncthreads() would also wait for the loads just
-    // issued); the asm statements keep LDS accesses on their side
+    // plain s_barrier (__syncthreads() would also wait for the loads in
+    // flight); the asm statements keep LDS accesses on their side
+    __builtin_amdgcn_sched_barrier(0);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
   };
+  auto stage_buf = [&](auto bi) -> Stage& {
+    constexpr int B = decltype(bi)::value & 3;
+    if constexpr (B == 0) return st0;
+    else if constexpr (B == 1) return st1;
+    else if constexpr (B == 2) return st2;
+    else return st3;
+  };
+  GroupScales gcur, gnext;  // scales of the current and of the next group
   const int ns = K / GK;
-  auto step = [&](Stage& cur, Stage& nxt, Scales& g, Scales& gnext, int c) __attribute__((always_inline)) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  // Step at position P (0..3) of the unrolled loop = stage c % 4.  The loads
+  // issued after stage c's: those of steps c - 2 and c - 1 (8 operand loads
+  // each, plus 12 scale loads at a group start, i.e. a step at position 0).
+  auto step = [&](auto pi, int c, auto steady) __attribute__((always_inline)) {
+    constexpr int P = decltype(pi)::value;
+    constexpr bool STEADY = decltype(steady)::value;  // every load of the step in range
+    constexpr int after = 2 * kOps + (P == 2 || P == 1 ? kScaleOps : 0);
+    if (STEADY) {
+      WAIT_VM(after);
+    } else {
+      if (c + 3 >= ns) __builtin_amdgcn_s_waitcnt(0x0F70);  // fewer loads in flight: wait for all
+      else WAIT_VM(after);
+    }
     barrier();
-    if (c + 1 < ns) issue(nxt, (c + 1) * GK);
-    if ((c & (GS - 1)) == 0 && c + GS < ns) issue_scales(gnext, (c + GS) * (GK / 32));
-    compute(cur, g, c & (GS - 1));
+    if (P == 0 && (STEADY || c + GS < ns)) load_scales(gnext, (c + GS) * (GK / 32));
+    if (STEADY || c + 3 < ns) issue(stage_buf(std::integral_constant<int, P + 3>{}), (c + 3) * GK);
+    compute(stage_buf(pi), gcur, P);
   };
-  issue_scales(sc0, 0);
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  load_scales(gcur, 0);
   issue(st0, 0);
-  for (int c = 0; c < ns; c += 2 * GS) {
-    step(st0, st1, sc0, sc1, c);
+  if (ns > 1) issue(st1, GK);
+  if (ns > 2) issue(st2, 2 * GK);
+  int c = 0;
+  // branch-free steady state: all loads of steps c .. c + 3 are in range
+  // (operand stages up to c + 6, scale group (c + 4) / 4)
+  for (; c + 7 <= ns; c += 4) {
+    const std::true_type S{};
+    step(I0{}, c, S);
+    step(I1{}, c + 1, S);
+    step(I2{}, c + 2, S);
+    step(I3{}, c + 3, S);
+    gcur = gnext;
+  }
+  for (; c < ns; c += 4) {
+    const std::false_type S{};
+    step(I0{}, c, S);
     if (c + 1 >= ns) break;
-    step(st1, st0, sc0, sc1, c + 1);
+    step(I1{}, c + 1, S);
     if (c + 2 >= ns) break;
-    step(st0, st1, sc0, sc1, c + 2);
+    step(I2{}, c + 2, S);
     if (c + 3 >= ns) break;
-    step(st1, st0, sc0, sc1, c + 3);
-    if (c + 4 >= ns) break;
-    step(st0, st1, sc1, sc0, c + 4);
-    if (c + 5 >= ns) break;
-    step(st1, st0, sc1, sc0, c + 5);
-    if (c + 6 >= ns) break;
-    step(st0, st1, sc1, sc0, c + 6);
-    if (c + 7 >= ns) break;
-    step(st1, st0, sc1, sc0, c + 7);
+    step(I3{}, c + 3, S);
+    gcur = gnext;
   }
 
   // ---- epilogue ---------------------------------------------------------
