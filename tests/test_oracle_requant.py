@@ -7,6 +7,7 @@ import os
 import numpy as np
 
 import oracle
+import synth
 from oracle.formats import E2M1_VALUES
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -121,3 +122,41 @@ def test_error_bound():
     b = oracle.dequant_fp4(d[0], s[0], 32, "ue8m0").reshape(32, 32, 32)
     step = 2.0 ** (s[0].astype(np.int64) - 127)[..., None]
     assert np.all(np.abs(a - b) <= step * 1.0)
+
+
+def requant_error_stats(src, sf, gs):
+    """Error of group16 -> group32 requantisation on one expert's matrix:
+    relative RMS and max error of the dequantised values, the share of
+    32-blocks whose two E4M3 scales are equal (where the group32 grid can
+    still hold the group16 values), and the share of elements that change."""
+    d, s = oracle.requant_g16_to_g32(src[None], sf[None], np.array([gs], np.float32))
+    a = oracle.dequant_fp4(src, sf, 16, "e4m3", gs)
+    b = oracle.dequant_fp4(d[0], s[0], 32, "ue8m0")
+    err = b - a
+    N, K = a.shape
+    blk_amax = np.abs(a).reshape(N, K // 32, 32).max(axis=2)
+    blk_err = np.abs(err).reshape(N, K // 32, 32).max(axis=2)
+    nz = blk_amax > 0
+    return {
+        "rel_rms": float(np.sqrt(np.mean(err ** 2) / np.mean(a ** 2))),
+        "max_err_over_block_amax": float((blk_err[nz] / blk_amax[nz]).max()),
+        "equal_scale_blocks": float(np.mean(sf[:, 0::2] == sf[:, 1::2])),
+        "changed": float(np.mean(err != 0)),
+    }
+
+
+def test_requant_accuracy_on_layer_weights():
+    """Accuracy of the requantisation on the synthetic decode16 layer's
+    weights (rows of one expert of w13 and of w2).  Per element the error is
+    at most half a step of the group32 grid, at most 2**e (the grid's largest
+    step is 2 units of 2**e); since the block maximum lies in (3, 6] units,
+    2**e < amax / 3.  The numbers printed here are the ones quoted as the
+    accuracy report."""
+    cfg = synth.REQUANT_CONFIGS["requant"]
+    for which, name in ((0, "w13"), (1, "w2")):
+        src, sf, gs = synth.make_requant_tensor(cfg, which, experts=[7])
+        st = requant_error_stats(src[0, :256], sf[0, :256], float(gs[0]))
+        print(f"requant accuracy {name}: " + ", ".join(f"{k} {v:.4f}" for k, v in st.items()))
+        assert st["max_err_over_block_amax"] < 1.0 / 3.0
+        # a fresh 2-bit-significand grid: a few percent to ~20% relative RMS
+        assert 0.01 < st["rel_rms"] < 0.3
