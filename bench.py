@@ -36,6 +36,8 @@ WORKLOAD_TEXT = {
     "decode16": "W4A16 NVFP4 decode: T=64 E=256 top-8 H=6144 I=2048, bf16 x, E2M1 + E4M3 k16 + fp32 global",
     "decode32": "FP8xFP4 decode: T=256 E=256 top-8 H=6144 I=2048, E4M3+UE8M0 k32 x, E2M1 + UE8M0 k32",
     "prefill32": "prefill: T=8192 E=256 top-8 Zipf(1.1) H=6144 I=2048, E4M3+UE8M0 k32 x, E2M1 + UE8M0 k32",
+    "prefill32_bf16q": "prefill: T=8192 E=256 top-8 Zipf(1.1) H=6144 I=2048, bf16 x quantised by the "
+                       "library to E4M3+UE8M0 k32, E2M1 + UE8M0 k32",
 }
 DTYPE = {"decode16": "f16", "decode32": "fp8xfp4", "prefill32": "fp8xfp4"}
 STAGES = ["route", "act_prep", "fc1_swiglu", "fc2", "combine"]
@@ -86,11 +88,13 @@ def gpu_forward_into(moe, torch, inp, d, ws, out):
     if ws is None:
         c = inp.cfg
         p = moe.make_problem(c.T, c.E, c.k, c.H, c.I, c.gran,
-                             moe.ACT_FP8_UE8M0_K32 if c.act == "fp8" else moe.ACT_BF16)
+                             {"fp8": moe.ACT_FP8_UE8M0_K32,
+                              "bf16q": moe.ACT_BF16_QUANT_FP8_K32}.get(c.act, moe.ACT_BF16))
         ws = torch.empty(moe.workspace_bytes(p), dtype=torch.uint8, device="cuda")
         out = torch.empty((c.T, c.H), dtype=torch.bfloat16, device="cuda")
     moe.forward(d["x"], d["topk_ids"], d["topk_w"], d["w13"], d["w13_sf"], d["w13_gs"], d["w2"],
-                d["w2_sf"], d["w2_gs"], inp.cfg.gran, x_sf=d["x_sf"], out=out, workspace=ws)
+                d["w2_sf"], d["w2_gs"], inp.cfg.gran, x_sf=d["x_sf"], out=out, workspace=ws,
+                quantize_x=inp.cfg.act == "bf16q")
     return ws, out
 
 
@@ -101,7 +105,7 @@ def stage_kernel(cfg, ids, stage):
     FP8 x FP4 GEMM or 64-row tiles)."""
     A = ids.size
     active = len(np.unique(ids[ids >= 0]))
-    mode = 2 if cfg.act == "fp8" else (0 if cfg.gran == 16 else 1)
+    mode = 2 if cfg.act in ("fp8", "bf16q") else (0 if cfg.gran == 16 else 1)
     gemm_ok = (mode == 2 and cfg.I % 512 == 0 and cfg.H % 512 == 0 and cfg.T * cfg.H < 2**31
                and A * cfg.I < 2**31 and cfg.I * cfg.H < 2**31)
     nt = (8 if gemm_ok else 4) if active and A / active > 16 else 1
@@ -132,6 +136,8 @@ def algorithmic_bytes(cfg, ids):
     w2 = H * I // 2 + H * I // g + gs
     if cfg.act == "bf16":
         x_bytes, h_bytes = T * H * 2, A * I * 2
+    elif cfg.act == "bf16q":
+        x_bytes, h_bytes = T * H * 2, A * I + A * I // 32
     else:
         x_bytes, h_bytes = T * H + T * H // 32, A * I + A * I // 32
     whole = active * (w13 + w2) + x_bytes + T * H * 2 + T * k * 8
@@ -335,12 +341,13 @@ def secondary(moe, torch, synth, args, inp16, d16):
                             "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
     del src13, sf13, gs13, src2, sf2, gs2, d13, s13, d2, s2
     torch.cuda.empty_cache()
-    for name in ("decode32", "prefill32"):
-        cfg = synth.CONFIGS[name]
+    for name in ("decode32", "prefill32", "prefill32_bf16q"):
+        cfg = (synth.CONFIGS[name] if name in synth.CONFIGS
+               else synth.variant(synth.CONFIGS["prefill32"], name=name, act="bf16q"))
         print(f"[bench] secondary {name}", file=sys.stderr, flush=True)
         inp = synth.make_moe_inputs(cfg)
         d = to_dev(torch, inp)
-        steps = 10 if name == "prefill32" else 20
+        steps = 10 if name.startswith("prefill") else 20
         ms_step, fwd_ms, stage_ms = run_forward_timed(moe, torch, inp, d, steps, 3)
         ab = algorithmic_bytes(cfg, inp.topk_ids)
         r = {"workload": WORKLOAD_TEXT[name], "ms_per_step": ms_step, "tokens_per_s": cfg.T / (ms_step * 1e-3),

@@ -19,12 +19,12 @@ import ctypes
 import os
 
 __all__ = ["Problem", "MoeFp4Error", "lib", "workspace_bytes", "route", "forward",
-           "requant_gran_k", "dropped_assignments", "LIB_PATH"]
+           "requant_gran_k", "quantize_act", "dropped_assignments", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoefp4.so")
 
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = range(5)
-ACT_BF16, ACT_FP8_UE8M0_K32 = 0, 1
+ACT_BF16, ACT_FP8_UE8M0_K32, ACT_BF16_QUANT_FP8_K32 = 0, 1, 2
 GATE_UP, UP_GATE = 0, 1
 
 
@@ -64,6 +64,8 @@ def lib():
         L.fp4_requant_gran_k.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _P, _P,
                                          ctypes.c_int32, _P, _P, _P, ctypes.c_int32, _P]
         L.fp4_requant_gran_k.restype = st
+        L.moe_fp4_quantize_act.argtypes = [ctypes.c_int64, ctypes.c_int64, _P, _P, _P, _P]
+        L.moe_fp4_quantize_act.restype = st
         L.moefp4_last_error.argtypes = []
         L.moefp4_last_error.restype = ctypes.c_char_p
         L.moefp4_set_stage_events.argtypes = [_P, ctypes.c_int32]
@@ -140,10 +142,13 @@ def route(problem: Problem, topk_ids, workspace=None, stream=None):
 
 
 def forward(x, topk_ids, topk_w, w13, w13_sf, w13_gs, w2, w2_sf, w2_gs, gran_k, x_sf=None,
-            w13_order="gate_up", out=None, workspace=None, stream=None, out_dtype=None):
+            w13_order="gate_up", out=None, workspace=None, stream=None, out_dtype=None,
+            quantize_x=False):
     """MoE forward on the GPU.  x: [T, H] bfloat16 (A16) or uint8/float8_e4m3fn
-    with x_sf [T, H/32] uint8 (A8).  Weights uint8 as in include/moefp4.h.
-    Returns out [T, H] bfloat16 (default) or float32 (out_dtype=torch.float32)."""
+    with x_sf [T, H/32] uint8 (A8); quantize_x=True with bfloat16 x asks the
+    library to quantise x to the A8 format first (act_fmt BF16_QUANT_FP8_K32).
+    Weights uint8 as in include/moefp4.h.  Returns out [T, H] bfloat16
+    (default) or float32 (out_dtype=torch.float32)."""
     import torch
     u8 = (torch.uint8,)
     fp8 = (torch.uint8, torch.float8_e4m3fn)
@@ -163,7 +168,10 @@ def forward(x, topk_ids, topk_w, w13, w13_sf, w13_gs, w2, w2_sf, w2_gs, gran_k, 
         out_dtype = torch.bfloat16 if out is None else out.dtype
     if out_dtype not in (torch.bfloat16, torch.float32):
         raise TypeError("out_dtype must be torch.bfloat16 or torch.float32")
-    p = make_problem(T, E, k, H, two_i // 2, gran_k, ACT_FP8_UE8M0_K32 if a8 else ACT_BF16, w13_order,
+    if quantize_x and a8:
+        raise ValueError("quantize_x takes bfloat16 x without x_sf")
+    act = ACT_FP8_UE8M0_K32 if a8 else (ACT_BF16_QUANT_FP8_K32 if quantize_x else ACT_BF16)
+    p = make_problem(T, E, k, H, two_i // 2, gran_k, act, w13_order,
                      OUT_F32 if out_dtype == torch.float32 else OUT_BF16)
     if out is None:
         out = torch.empty((T, H), dtype=out_dtype, device=x.device)
@@ -195,6 +203,22 @@ def requant_gran_k(src, src_sf, src_gs=None, src_gran=16, dst_gran=32, dst=None,
     _check(lib().fp4_requant_gran_k(E, N, K, _ptr(src), _ptr(src_sf), src_gran, _ptr(src_gs),
                                     _ptr(dst), _ptr(dst_sf), dst_gran, _stream(stream)))
     return dst, dst_sf
+
+
+def quantize_act(x, x_fp8=None, x_sf=None, stream=None):
+    """bfloat16 [T, H] -> (E4M3 codes [T, H] uint8, UE8M0 scales [T, H/32]
+    uint8), per 32 elements (moe_fp4_quantize_act)."""
+    import torch
+    _dev(x, "x", (torch.bfloat16, torch.int16, torch.uint16))
+    T, H = x.shape
+    if x_fp8 is None:
+        x_fp8 = torch.empty((T, H), dtype=torch.uint8, device=x.device)
+    if x_sf is None:
+        x_sf = torch.empty((T, H // 32), dtype=torch.uint8, device=x.device)
+    _dev(x_fp8, "x_fp8", (torch.uint8,))
+    _dev(x_sf, "x_sf", (torch.uint8,))
+    _check(lib().moe_fp4_quantize_act(T, H, _ptr(x), _ptr(x_fp8), _ptr(x_sf), _stream(stream)))
+    return x_fp8, x_sf
 
 
 def set_stage_events(events_array, n: int):

@@ -41,10 +41,10 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
   size_t flags, counts, offsets, sorted, slot_of, tiles, ntiles;
-  size_t act_scale, x16, hmax, h, h_sf, y, route_hist, total;
+  size_t act_scale, x16, x8, x8_sf, hmax, h, h_sf, y, route_hist, total;
   int route_chunks, route_chunk;
   int tile_m, nt, max_tiles;
-  bool a8, g16_a16;
+  bool a8, quant_x, g16_a16;
 };
 
 moefp4_status check_problem(const moefp4_problem* p) {
@@ -58,7 +58,8 @@ moefp4_status check_problem(const moefp4_problem* p) {
   if (p->H <= 0 || p->I <= 0) return fail(MOEFP4_EINVAL, "H and I must be positive");
   if (p->gran_k != 16 && p->gran_k != 32)
     return fail(MOEFP4_EINVAL, "gran_k must be 16 or 32, got %d", p->gran_k);
-  if (p->act_fmt != MOEFP4_ACT_BF16 && p->act_fmt != MOEFP4_ACT_FP8_UE8M0_K32)
+  if (p->act_fmt != MOEFP4_ACT_BF16 && p->act_fmt != MOEFP4_ACT_FP8_UE8M0_K32 &&
+      p->act_fmt != MOEFP4_ACT_BF16_QUANT_FP8_K32)
     return fail(MOEFP4_EINVAL, "unknown act_fmt %d", p->act_fmt);
   if (p->w13_order != MOEFP4_GATE_UP && p->w13_order != MOEFP4_UP_GATE)
     return fail(MOEFP4_EINVAL, "unknown w13_order %d", p->w13_order);
@@ -67,7 +68,7 @@ moefp4_status check_problem(const moefp4_problem* p) {
   if (p->H % 32 || p->I % 32)
     return fail(MOEFP4_EINVAL, "H and I must be multiples of 32 (K blocks of the scale grid), got H=%d I=%d",
                 p->H, p->I);
-  if (p->act_fmt == MOEFP4_ACT_FP8_UE8M0_K32 && p->gran_k == 16)
+  if (p->act_fmt != MOEFP4_ACT_BF16 && p->gran_k == 16)
     return fail(MOEFP4_EUNSUPPORTED,
                 "FP8 activations with group16 weights (recipe (1,1,16)) are not computed: requantise the "
                 "weights to group32 with fp4_requant_gran_k");
@@ -83,7 +84,8 @@ moefp4_status plan(const moefp4_problem* p, Layout* L) {
   moefp4_status st = check_problem(p);
   if (st != MOEFP4_OK) return st;
   const size_t A = (size_t)p->T * p->top_k, E = p->E, T = p->T, H = p->H, I = p->I;
-  L->a8 = p->act_fmt == MOEFP4_ACT_FP8_UE8M0_K32;
+  L->quant_x = p->act_fmt == MOEFP4_ACT_BF16_QUANT_FP8_K32;
+  L->a8 = p->act_fmt == MOEFP4_ACT_FP8_UE8M0_K32 || L->quant_x;
   L->g16_a16 = !L->a8 && p->gran_k == 16;
   const size_t active = A < E ? A : E;
   const double avg = active ? (double)A / (double)active : 0.0;
@@ -107,6 +109,8 @@ moefp4_status plan(const moefp4_problem* p, Layout* L) {
   L->ntiles = take(4);
   L->act_scale = take(L->g16_a16 ? T * 4 : 0);
   L->x16 = take(L->g16_a16 && L->nt != 1 ? T * H * 2 : 0);
+  L->x8 = take(L->quant_x ? T * H : 0);
+  L->x8_sf = take(L->quant_x ? T * (H / 32) : 0);
   L->hmax = take(L->g16_a16 ? A * 4 : 0);
   L->h = take(L->a8 ? A * I : A * I * 2);
   L->h_sf = take(L->a8 ? A * (I / 32) : 0);
@@ -137,7 +141,7 @@ moefp4_status hip_status(hipError_t e, const char* what) {
 moefp4_status route_into(const moefp4_problem* p, const Layout& L, const int32_t* ids,
                          int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* slot_of,
                          void* ws, uint32_t* zero_words, int n_zero, const void* x, float* row_scale,
-                         hipStream_t s) {
+                         uint8_t* x8, uint8_t* x8_sf, hipStream_t s) {
   moefp4::RouteOut o;
   o.counts = counts;
   o.offsets = offsets;
@@ -152,6 +156,8 @@ moefp4_status route_into(const moefp4_problem* p, const Layout& L, const int32_t
   o.T = p->T;
   o.H = p->H;
   o.row_scale = row_scale;
+  o.x8 = x8;
+  o.xsf = x8_sf;
   o.nchunks = L.route_chunks;
   o.chunk = L.route_chunk;
   o.hist = L.route_chunks ? at<int32_t>(ws, L.route_hist) : nullptr;
@@ -184,7 +190,7 @@ moefp4_status moe_fp4_route(const moefp4_problem* p, const int32_t* topk_ids, in
     return fail(MOEFP4_EWORKSPACE, "workspace of %zu bytes needed, got %zu", L.total,
                 workspace ? ws_bytes : (size_t)0);
   st = route_into(p, L, topk_ids, counts, offsets, sorted_assign, slot_of, workspace, nullptr, 0,
-                  nullptr, nullptr, stream);
+                  nullptr, nullptr, nullptr, nullptr, stream);
   return st == MOEFP4_OK ? ok() : st;
 }
 
@@ -199,8 +205,9 @@ moefp4_status moe_fp4_forward(const moefp4_problem* p, const void* x, const uint
   if (p->T == 0) return ok();
   if (!x || !topk_ids || !topk_w || !w13 || !w13_sf || !w2 || !w2_sf || !out)
     return fail(MOEFP4_EINVAL, "x, topk_ids, topk_w, w13, w13_sf, w2, w2_sf and out must be non-NULL");
-  if (L.a8 && !x_sf) return fail(MOEFP4_EINVAL, "FP8 activations need x_sf");
-  if (!L.a8 && x_sf) return fail(MOEFP4_EINVAL, "x_sf must be NULL for bfloat16 activations");
+  if (L.a8 && !L.quant_x && !x_sf) return fail(MOEFP4_EINVAL, "FP8 activations need x_sf");
+  if ((!L.a8 || L.quant_x) && x_sf)
+    return fail(MOEFP4_EINVAL, "x_sf must be NULL for bfloat16 activations");
   if (misaligned(x, 16) || misaligned(w13, 16) || misaligned(w2, 16) || misaligned(out, 16) ||
       misaligned(w13_sf, 16) || misaligned(w2_sf, 16) || (x_sf && misaligned(x_sf, 16)))
     return fail(MOEFP4_EINVAL, "x, x_sf, w13, w13_sf, w2, w2_sf and out must be 16-byte aligned");
@@ -220,8 +227,13 @@ moefp4_status moe_fp4_forward(const moefp4_problem* p, const void* x, const uint
   // computes the per-token fp16 staging scales, and FC1 converts while staging
   const bool stage_f16 = L.g16_a16 && L.nt == 1;
   float* xs = L.g16_a16 ? at<float>(workspace, L.act_scale) : nullptr;
+  // bf16 x to be quantised to FP8 + UE8M0 per 32: also done by the route
+  // launch, into the workspace
+  uint8_t* x8 = L.quant_x ? at<uint8_t>(workspace, L.x8) : nullptr;
+  uint8_t* x8_sf = L.quant_x ? at<uint8_t>(workspace, L.x8_sf) : nullptr;
   st = route_into(p, L, topk_ids, counts, offsets, sorted, slot_of, workspace, hmax,
-                  L.g16_a16 ? A : 0, stage_f16 ? x : nullptr, stage_f16 ? xs : nullptr, stream);
+                  L.g16_a16 ? A : 0, (stage_f16 || L.quant_x) ? x : nullptr,
+                  stage_f16 ? xs : nullptr, x8, x8_sf, stream);
   if (st != MOEFP4_OK) return st;
   stage_mark(1, stream);
 
@@ -245,8 +257,8 @@ moefp4_status moe_fp4_forward(const moefp4_problem* p, const void* x, const uint
   a.N = 2 * p->I;
   a.h_out = at<void>(workspace, L.h);
   if (L.a8) {
-    a.act = x;
-    a.act_sf = x_sf;
+    a.act = L.quant_x ? x8 : x;
+    a.act_sf = L.quant_x ? x8_sf : x_sf;
     a.h_sf_out = at<uint8_t>(workspace, L.h_sf);
     stage_mark(2, stream);
     st = hip_status(L.nt == 1   ? moefp4::launch_fc_decode(a, 2, true, L.max_tiles, stream)
@@ -343,6 +355,20 @@ moefp4_status fp4_requant_gran_k(int64_t E, int64_t N, int64_t K, const uint8_t*
     }
   moefp4_status st = hip_status(
       moefp4::launch_requant_g16_g32(src, src_sf, src_gs, dst, dst_sf, E, N, K, stream), "requant");
+  return st == MOEFP4_OK ? ok() : st;
+}
+
+moefp4_status moe_fp4_quantize_act(int64_t T, int64_t H, const void* x, uint8_t* x_fp8,
+                                   uint8_t* x_sf, hipStream_t stream) {
+  if (T < 0 || H <= 0 || H % 32) return fail(MOEFP4_EINVAL, "need T >= 0 and H a positive multiple of 32, got T=%lld H=%lld", (long long)T, (long long)H);
+  if (H > (1 << 30) || T > (1ll << 40) / H) return fail(MOEFP4_EUNSUPPORTED, "T*H too large");
+  if (T == 0) return ok();
+  if (!x || !x_fp8 || !x_sf) return fail(MOEFP4_EINVAL, "x, x_fp8 and x_sf must be non-NULL");
+  if (misaligned(x, 16) || misaligned(x_fp8, 16))
+    return fail(MOEFP4_EINVAL, "x and x_fp8 must be 16-byte aligned");
+  moefp4_status st = hip_status(moefp4::launch_quantize_act(static_cast<const uint16_t*>(x), T, (int)H,
+                                                            x_fp8, x_sf, stream),
+                                "quantize_act");
   return st == MOEFP4_OK ? ok() : st;
 }
 

@@ -27,6 +27,10 @@ struct RouteOut {
   const uint16_t* x;
   int T, H;
   float* row_scale;
+  // optional: FP8 + UE8M0 per 32 quantisation of bf16 rows x [T, H] into
+  // x8 [T, H] and xsf [T, H/32] (x8 null: not computed)
+  uint8_t* x8;
+  uint8_t* xsf;
   // multi-workgroup form (nchunks > 0): chunks of `chunk` assignments and a
   // [nchunks][E + 1] int32 scratch for their histograms / starts
   int nchunks, chunk;
@@ -44,6 +48,12 @@ inline int route_chunk(long long A) {
 
 hipError_t launch_route(const int32_t* topk_ids, int A, int E, int tile_m, const RouteOut& o,
                         hipStream_t s);
+
+// bf16 [T, H] -> E4M3 [T, H] + UE8M0 [T, H/32]: per 32 elements e =
+// ceil(log2(amax / 448)) (amax == 0: e = -127), clamped to [-127, 127],
+// codes RNE(x / 2**e), sign kept.  H % 32 == 0.
+hipError_t launch_quantize_act(const uint16_t* x, long long T, int H, uint8_t* x8, uint8_t* xsf,
+                               hipStream_t s);
 
 // bf16 [T, H] -> fp16 [T, H] * 2**-p_t with p_t chosen per row so the row
 // maximum lands in [2**14, 2**15); scale[t] = 2**p_t.

@@ -152,6 +152,72 @@ __device__ int finish_counts(int c, int E, int tile_m, int drops, int* s_tmp, in
 }
 
 // Single-workgroup route (small T * k): histogram, scans, stable scatter.
+// FP8 quantisation of one 32-element block of a bf16 row (the activation
+// side of recipe (1, 1, 32)): UE8M0 e = smallest with 448 * 2**e >= amax,
+// E4M3 RNE of x / 2**e (x / 2**e is exact in FP32: x has 8 significant bits
+// and |x / 2**e| <= 448; values too small for FP32 normals round to zero
+// in E4M3 either way).
+__device__ __forceinline__ void quantize_block32(const uint16_t* __restrict__ src, uint8_t* dst,
+                                                 uint8_t* sf) {
+  uint4 v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = reinterpret_cast<const uint4*>(src)[i];
+  uint32_t m = 0;  // largest magnitude, as bf16 bits (monotone in the value)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t lo = w[j] & 0x7FFFu, hi = (w[j] >> 16) & 0x7FFFu;
+      m = lo > m ? lo : m;
+      m = hi > m ? hi : m;
+    }
+  }
+  int ex = m ? ceil_log2_over_448(bf16_to_f32(m)) : -127;
+  ex = ex < -127 ? -127 : (ex > 127 ? 127 : ex);
+  const float inv = __builtin_ldexpf(1.0f, -ex);
+  uint32_t q[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+    for (int j = 0; j < 4; j += 2) {
+      const uint32_t c0 = f32_to_e4m3_rne(bf16_to_f32(w[j] & 0xFFFFu) * inv);
+      const uint32_t c1 = f32_to_e4m3_rne(bf16_to_f32(w[j] >> 16) * inv);
+      const uint32_t c2 = f32_to_e4m3_rne(bf16_to_f32(w[j + 1] & 0xFFFFu) * inv);
+      const uint32_t c3 = f32_to_e4m3_rne(bf16_to_f32(w[j + 1] >> 16) * inv);
+      q[2 * i + j / 2] = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+    }
+  }
+  reinterpret_cast<uint4*>(dst)[0] = uint4{q[0], q[1], q[2], q[3]};
+  reinterpret_cast<uint4*>(dst)[1] = uint4{q[4], q[5], q[6], q[7]};
+  *sf = (uint8_t)(ex + 127);
+}
+
+// Workgroup b of nb quantises 32-element blocks b * 1024 + tid, then every
+// nb * 1024 further.
+__device__ void quantize_rows_from(const uint16_t* __restrict__ x, long long T, int H,
+                                   uint8_t* __restrict__ x8, uint8_t* __restrict__ xsf, int b,
+                                   int nb) {
+  const long long nblk = T * (H / 32);
+  for (long long i = (long long)b * kRouteThreads + threadIdx.x; i < nblk;
+       i += (long long)nb * kRouteThreads)
+    quantize_block32(x + i * 32, x8 + i * 32, xsf + i);
+}
+
+__global__ __launch_bounds__(kRouteThreads) void quantize_act_kernel(const uint16_t* __restrict__ x,
+                                                                     long long T, int H,
+                                                                     uint8_t* __restrict__ x8,
+                                                                     uint8_t* __restrict__ xsf) {
+  quantize_rows_from(x, T, H, x8, xsf, blockIdx.x, gridDim.x);
+}
+
+// Activation preparation done by the extra workgroups of a route launch.
+__device__ void row_prep(const RouteOut& o, int b, int nb) {
+  if (o.row_scale) row_scales_from(o, b, nb);
+  if (o.x8) quantize_rows_from(o.x, o.T, o.H, o.x8, o.xsf, b, nb);
+}
+
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t* __restrict__ ids,
                                                               int A, int E, int tile_m,
                                                               RouteOut o) {
@@ -164,7 +230,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t* __r
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // workgroups past the first compute the per-row staging scales instead
   if (blockIdx.x > 0) {
-    row_scales_from(o, blockIdx.x - 1, gridDim.x - 1);
+    row_prep(o, blockIdx.x - 1, gridDim.x - 1);
     return;
   }
 
@@ -201,7 +267,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_hist_kernel(const int32_t
   __shared__ int s_drop;
   const int tid = threadIdx.x;
   if (blockIdx.x >= o.nchunks) {
-    row_scales_from(o, blockIdx.x - o.nchunks, gridDim.x - o.nchunks);
+    row_prep(o, blockIdx.x - o.nchunks, gridDim.x - o.nchunks);
     return;
   }
   for (int e = tid; e < E; e += kRouteThreads) s_cnt[e] = 0;
@@ -299,6 +365,10 @@ hipError_t launch_route(const int32_t* topk_ids, int A, int E, int tile_m, const
     scale_blocks = (o.T + kRouteWaves - 1) / kRouteWaves;
     scale_blocks = scale_blocks > 256 ? 256 : scale_blocks;
   }
+  if (o.x8 && o.T > 0) {
+    const long long nb = ((long long)o.T * (o.H / 32) + kRouteThreads - 1) / kRouteThreads;
+    scale_blocks = (int)(nb > 256 ? 256 : nb);
+  }
   if (o.nchunks <= 0) {
     hipLaunchKernelGGL(route_kernel, dim3(1 + scale_blocks), dim3(kRouteThreads), lds, s, topk_ids, A,
                        E, tile_m, o);
@@ -313,6 +383,16 @@ hipError_t launch_route(const int32_t* topk_ids, int A, int E, int tile_m, const
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(route_scatter_kernel, dim3(o.nchunks), dim3(kRouteThreads), lds, s, topk_ids, A,
                      E, o);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_act(const uint16_t* x, long long T, int H, uint8_t* x8, uint8_t* xsf,
+                               hipStream_t s) {
+  if (T <= 0 || H <= 0) return hipSuccess;
+  long long nb = (T * (H / 32) + kRouteThreads - 1) / kRouteThreads;
+  nb = nb > 1024 ? 1024 : nb;
+  hipLaunchKernelGGL(quantize_act_kernel, dim3((unsigned)nb), dim3(kRouteThreads), 0, s, x, T, H, x8,
+                     xsf);
   return hipGetLastError();
 }
 

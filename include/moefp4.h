@@ -56,8 +56,15 @@ typedef enum moefp4_status {
  * BF16: x [T, H] bfloat16.
  * FP8_UE8M0_K32: x [T, H] E4M3 (fn) bytes and x_sf [T, H/32] UE8M0 bytes,
  *   value = fp8 * 2**(sf - 127) -- the activation side of the FP8xFP4
- *   recipe (1, 1, 32) of [P2] Context. */
-typedef enum moefp4_act_fmt { MOEFP4_ACT_BF16 = 0, MOEFP4_ACT_FP8_UE8M0_K32 = 1 } moefp4_act_fmt;
+ *   recipe (1, 1, 32) of [P2] Context.
+ * BF16_QUANT_FP8_K32: x [T, H] bfloat16, quantised by the library to the
+ *   FP8_UE8M0_K32 format (as moe_fp4_quantize_act) before the FP8xFP4
+ *   computation; x_sf must be NULL. */
+typedef enum moefp4_act_fmt {
+  MOEFP4_ACT_BF16 = 0,
+  MOEFP4_ACT_FP8_UE8M0_K32 = 1,
+  MOEFP4_ACT_BF16_QUANT_FP8_K32 = 2
+} moefp4_act_fmt;
 
 /* Order of the 2I rows of w13.  GATE_UP: rows [0, I) are the gate projection
  * (the kernel-native "w31"/"gate_up" of [P3] _normalize_w13_layout).
@@ -140,6 +147,19 @@ moefp4_status fp4_requant_gran_k(int64_t E, int64_t N, int64_t K,
                                  int32_t src_gran, const float* src_gs,
                                  uint8_t* dst, uint8_t* dst_sf, int32_t dst_gran,
                                  hipStream_t stream);
+
+/* Quantise bfloat16 activation rows to the FP8 activation format of recipe
+ * (1, 1, 32) ([P2] Context): per row, per 32 consecutive elements, UE8M0
+ * scale byte e + 127 with e the smallest integer such that 448 * 2**e >=
+ * max |x| (a block of zeros gets byte 0; e clamped to [-127, 127]), and
+ * E4M3 (fn) codes round-to-nearest-even of x / 2**e, the sign kept (also on
+ * zero).  The same rule quantises h between FC1 and FC2 on the FP8 path.
+ * x [T, H] bfloat16, x_fp8 [T, H] uint8, x_sf [T, H/32] uint8, all device
+ * memory owned by the caller, x and x_fp8 16-byte aligned; H a positive
+ * multiple of 32 (EINVAL otherwise).  Enqueued on `stream`.  NaN and
+ * infinite inputs are outside the contract. */
+moefp4_status moe_fp4_quantize_act(int64_t T, int64_t H, const void* x, uint8_t* x_fp8,
+                                   uint8_t* x_sf, hipStream_t stream);
 
 /* Profiling hook.  With events non-NULL and n >= 6, each later
  * moe_fp4_forward call on this thread records, on its stream, events[0]

@@ -30,7 +30,7 @@ def L():
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
     assert {"moe_fp4_forward", "moe_fp4_route", "fp4_requant_gran_k", "moe_fp4_workspace_bytes",
-            "moefp4_last_error", "moefp4_version"} <= set(names)
+            "moe_fp4_quantize_act", "moefp4_last_error", "moefp4_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
     assert b"gfx950" in L.moefp4_version()
@@ -64,6 +64,7 @@ def test_workspace_sizes(L):
     (dict(I=2000), m.EINVAL),
     (dict(I=2080), m.EUNSUPPORTED),
     (dict(act_fmt=1, gran_k=16), m.EUNSUPPORTED),
+    (dict(act_fmt=2, gran_k=16), m.EUNSUPPORTED),
     (dict(act_fmt=7), m.EINVAL),
     (dict(w13_order=3), m.EINVAL),
     (dict(out_fmt=2), m.EINVAL),
@@ -105,3 +106,24 @@ def test_requant_rejects_before_launch(L):
     assert rq(2, 4, 64, f, f, 16, z, ctypes.c_void_p(1 << 24), g, 32, z) == m.EINVAL  # src_sf overlaps src
     assert rq(0, 4, 64, z, z, 16, z, z, z, 32, z) == 0                   # empty
     assert rq(2, 4, 64, ctypes.c_void_p((1 << 20) + 8), g, 16, z, f, ctypes.c_void_p(1 << 31), 32, z) == m.EINVAL
+
+
+def test_quantize_act_rejects_before_launch(L):
+    z = ctypes.c_void_p(0)
+    f = ctypes.c_void_p(1 << 20)
+    g = ctypes.c_void_p(1 << 30)
+    q = L.moe_fp4_quantize_act
+    assert q(4, 48, f, g, f, z) == m.EINVAL                       # H % 32
+    assert q(4, 0, f, g, f, z) == m.EINVAL
+    assert q(-1, 64, f, g, f, z) == m.EINVAL
+    assert q(4, 64, z, g, f, z) == m.EINVAL                       # NULL x
+    assert q(4, 64, ctypes.c_void_p((1 << 20) + 8), g, f, z) == m.EINVAL  # misaligned x
+    assert q(0, 64, z, z, z, z) == 0                              # empty
+
+
+def test_forward_quant_x_rejects_x_sf(L):
+    p = P(gran_k=32, act_fmt=2)
+    f = ctypes.c_void_p(1 << 20)
+    z = ctypes.c_void_p(0)
+    st = L.moe_fp4_forward(ctypes.byref(p), f, f, f, f, f, f, z, f, f, z, f, f, 1 << 40, z)
+    assert st == m.EINVAL and b"x_sf" in L.moefp4_last_error()
