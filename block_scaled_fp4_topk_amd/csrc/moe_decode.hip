@@ -1,61 +1,74 @@
-// Decode-shaped grouped GEMMs, occupancy-driven form: FC1 + SwiGLU (+ h
-// quantisation) and FC2 for tiles of at most 16 activation rows per expert.
+// Decode-shaped grouped GEMMs: FC1 + SwiGLU (+ h quantisation) and FC2 for
+// expert tiles of at most 16 activation rows.
 //   MODE 0  bf16 activations, group16 E4M3 weights   -> fp16 MFMA
 //   MODE 1  bf16 activations, group32 UE8M0 weights  -> bf16 MFMA
 //   MODE 2  FP8 + UE8M0 activations, group32 weights -> block-scaled MFMA
 // (the W4A16 forms of b12x moe/fused/w4a16/prepare.py and the FP8xFP4
 // recipe (1, 1, 32) of the GLM-5.2 NVFP4 group16 MegaMoE notes, Context).
 //
-// Decode is a weight stream.  This kernel keeps HBM busy by residency rather
-// than by software pipelining: each wave holds only one 256-element K chunk
-// (32 code bytes per lane per 16-row tile) and few registers, so 8 waves
-// per SIMD are resident and the memory latency of one wave is covered by
-// the others.  Per chunk: every thread issues its share of the activation
-// tile (16 rows, staged once in LDS for the 4 waves) and its weight loads,
-// one barrier, the MFMAs, one barrier.
+// Decode is a weight stream, so the kernel is built around how the weight
+// bytes leave HBM.  A workgroup owns 128 weight rows of one expert (FC1: 64
+// gate + the matching 64 up rows; FC2: 128 output rows) and walks K in
+// 256-element chunks (128 code bytes per row).  Each chunk's 16 KB of codes
+// goes straight to LDS with 16-byte direct-to-LDS loads marked non-temporal,
+// every load instruction covering eight whole 128-byte rows (measured on the
+// decode16 FC1 geometry: 6.8 TB/s for this form against 6.1 TB/s for
+// register loads in the MFMA lane layout, which can only ask for 64 bytes
+// of each row per instruction).  The block scales stream the same way, one
+// 128-byte line per row per scale group (8 chunks of group16 scales or 16
+// chunks of group32 scales): the next group's lines arrive a slice per
+// chunk, and at the start of a group every lane copies its own scale bytes
+// of all the group's chunks into registers, which frees the buffer.
+// Activation rows that hold a token are loaded into registers one chunk
+// ahead and staged in LDS once for the 4 waves (bf16 -> fp16 x 2**-p for
+// group16 weights, exact).
 //
-// Load shapes: the 4 lanes of a weight row read 64 contiguous bytes per
-// instruction and two instructions cover the row's 128-byte chunk (cached
-// loads, so the second hits the line the first brought in).  Rows of a tile
-// past the expert's token count read activation row 0 (their MFMA columns
-// are never stored).
+// Per chunk: stage the activations, barrier, read every operand of the
+// chunk into registers, barrier, issue the next chunk's loads, MFMAs.  Three
+// workgroups per CU (41 KB of LDS each) keep loads in flight while others
+// read and compute.
+//
 // K index permutation inside a chunk (identical for both MFMA operands):
-//  16-bit MFMA j = 0..7 of lane group q takes chunk elements
-//    [128 (j / 4) + 32 q + 8 (j % 4), + 8);
-//  scaled MFMA step st = 0, 1 covers [128 st, 128 st + 128) in the measured
-//    FP4 / FP8 lane layouts (see common.h).
+// lane group q (= lane / 16) holds code bytes [32 q, 32 q + 32) of a row,
+// i.e. K [64 q, 64 q + 64):
+//   16-bit MFMA j = 0..7 takes K [64 q + 8 j, + 8) (code dword j);
+//   scaled MFMA step st = 0, 1: hardware K block b of the step is memory K
+//   block 2 b + st (32 elements), so the FP4 operand of lane group q is code
+//   bytes [32 q + 16 st, + 16) and the FP8 operand lane group q takes the
+//   16-element halves of memory blocks 2 (q / 2) + st and 4 + 2 (q / 2) + st
+//   selected by q % 2 (the FP8 lane layout of common.h).
 #include "common.h"
 #include "kernels.h"
-
-#include <type_traits>
 
 namespace moefp4 {
 
 namespace {
 
-constexpr int KC = 256;
-// chunks per weight-scale staging group: one full 128-byte line of a row's
-// scales at a time (group16: 16 B per row per chunk -> 8 chunks; group32:
-// 8 B -> 16 chunks); half-line groups measured 3-12% slower
+constexpr int KC = 256;   // K elements per chunk
+constexpr int WR = 128;   // weight rows per workgroup
+constexpr int kNT = 2;    // cache policy of the weight / scale loads: non-temporal
 
 __device__ __forceinline__ uint32_t dw(const uint4& v, int r) {
   return r == 0 ? v.x : r == 1 ? v.y : r == 2 ? v.z : v.w;
 }
 
+// 16-byte segment swizzle of a staged scale line: row lr keeps logical
+// segment s at s ^ sc_swz(lr), so the 16 lanes reading one dword of 16
+// consecutive rows hit 16 distinct bank groups
+__device__ __forceinline__ int sc_swz(int lr) { return (lr >> 1) & 7; }
 
 template <int MODE, bool FC1>
-__global__ __launch_bounds__(256, 8) void fc_decode_kernel(FcArgs a) {
-  constexpr int ESZ = MODE == 2 ? 1 : 2;          // activation element bytes
-  constexpr int ROWB = KC * ESZ + 16;             // staged row stride (bytes)
-  constexpr int SEGB = KC * ESZ / 16;             // bytes staged per thread (32 or 16)
-  constexpr int SCB = MODE == 0 ? KC / 16 : KC / 32;  // weight-scale bytes per row per chunk
-  constexpr int SG = MODE == 0 ? 8 : 16;
-  constexpr int SCROW = SG * SCB + (MODE == 0 ? 16 : 8);  // staged scale row stride (bytes)
-  using ScPiece = typename std::conditional<MODE == 0, uint4, uint2>::type;
-  __shared__ __attribute__((aligned(16))) uint8_t s_b[16 * ROWB];
+__global__ __launch_bounds__(256, 3) void fc_decode_kernel(FcArgs a) {
+  constexpr int ESZ = MODE == 2 ? 1 : 2;               // activation element bytes
+  constexpr int AROW = KC * ESZ + 16;                  // staged activation row stride
+  constexpr int SEGB = KC * ESZ / 16;                  // activation bytes per thread (32 or 16)
+  constexpr int SCB = MODE == 0 ? KC / 16 : KC / 32;   // weight-scale bytes per row per chunk
+  constexpr int SG = 128 / SCB;                        // chunks per scale group
+  constexpr int RPC = WR / SG;                         // scale lines staged per chunk (16 or 8)
+  __shared__ __attribute__((aligned(16))) uint8_t s_w[WR * 128];
+  __shared__ __attribute__((aligned(16))) uint8_t s_sc[WR * 128];
+  __shared__ __attribute__((aligned(16))) uint8_t s_b[16 * AROW];
   __shared__ __attribute__((aligned(16))) uint8_t s_bsf[16 * 8];
-  // weight scales of 4 chunks for the workgroup's 128 rows (padded rows)
-  __shared__ __attribute__((aligned(16))) uint8_t s_sc[128 * SCROW];
   __shared__ int s_src[16];
   __shared__ float s_rs[16];
   __shared__ float s_amax[4][16];
@@ -64,23 +77,72 @@ __global__ __launch_bounds__(256, 8) void fc_decode_kernel(FcArgs a) {
   if (tile >= a.ntiles[0]) return;
   const int e = a.tiles[2 * tile], m0 = a.tiles[2 * tile + 1];
   const int ne = a.counts[e], oe = a.offsets[e];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, q = lane >> 4;
   const int K = a.K, N = a.N;
+  const int nchunks = K / KC;
+  const int ngroups = (nchunks + SG - 1) / SG;
+  const size_t rowb = (size_t)(K >> 1);          // code bytes per weight row
+  const int sb = K / (MODE == 0 ? 16 : 32);       // scale bytes per weight row
+  const uint8_t* wexp = a.w + (size_t)e * N * rowb;
+  const uint8_t* sexp = a.wsf + (size_t)e * N * sb;
 
-  int obase, row0, row1;
-  if (FC1) {
-    obase = blockIdx.x * 64 + wave * 16;
-    row0 = a.w13_order == 0 ? obase + r16 : a.I + obase + r16;  // gate
-    row1 = a.w13_order == 0 ? a.I + obase + r16 : obase + r16;  // up
-  } else {
-    obase = blockIdx.x * 128 + wave * 32;
-    row0 = obase + r16;
-    row1 = obase + 16 + r16;
+  // workgroup-local weight row (0..127) -> row of the expert's matrix
+  auto wrow = [&](int lr) __attribute__((always_inline)) -> int {
+    if (FC1) {
+      const int i0 = blockIdx.x * 64 + (lr & 63);
+      return ((lr >= 64) != (a.w13_order != 0)) ? a.I + i0 : i0;
+    }
+    return blockIdx.x * 128 + lr;
+  };
+
+  // weight loads: instruction i of a wave covers rows 32 wave + 8 i .. + 8;
+  // lane -> row + lane / 8, LDS slot lane % 8 holding the row's 16-byte
+  // segment (lane % 8) ^ (row % 8)
+  const uint8_t* wsrc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int lr = 32 * wave + 8 * i + (lane >> 3);
+    wsrc[i] = wexp + (size_t)wrow(lr) * rowb + 16 * ((lane & 7) ^ (lr & 7));
   }
-  const size_t rb = (size_t)(K >> 1), sb = (size_t)(K / (MODE == 0 ? 16 : 32));
-  const uint8_t* wc0 = a.w + ((size_t)e * N + row0) * rb + 16 * q;
-  const uint8_t* wc1 = a.w + ((size_t)e * N + row1) * rb + 16 * q;
+  auto issue_w = [&](int c) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds(wsrc[i] + (size_t)c * 128, &s_w[(32 * wave + 8 * i) * 128], 16, 0,
+                                       kNT);
+  };
+  // scale loads: this wave's rows [rb0, rb0 + nrows) of group g's 128-byte
+  // lines, 16 bytes per lane (8 rows per instruction) when the scale rows
+  // are 16-byte aligned, else 4 bytes (2 rows); bytes past a row's scales
+  // are not read
+  const bool sc16 = (sb & 15) == 0;
+  auto issue_sc = [&](int g, int rb0, int nrows) __attribute__((always_inline)) {
+    if (sc16) {
+      for (int r = rb0; r < rb0 + nrows; r += 8) {
+        const int lr = r + (lane >> 3);
+        const int off = 128 * g + 16 * ((lane & 7) ^ sc_swz(lr));
+        if (off < sb)
+          __builtin_amdgcn_global_load_lds(sexp + (size_t)wrow(lr) * sb + off, &s_sc[r * 128], 16, 0, kNT);
+      }
+    } else {
+      for (int r = rb0; r < rb0 + nrows; r += 2) {
+        const int lr = r + (lane >> 5);
+        const int off = 128 * g + 4 * ((lane & 31) ^ (4 * sc_swz(lr)));
+        if (off < sb)
+          __builtin_amdgcn_global_load_lds(sexp + (size_t)wrow(lr) * sb + off, &s_sc[r * 128], 4, 0, kNT);
+      }
+    }
+  };
+  // the slice of group g's lines staged while chunk j (0..SG-1) of the group
+  // before it runs: rows [j RPC, (j + 1) RPC), split over the waves
+  auto issue_sc_slice = [&](int g, int j) __attribute__((always_inline)) {
+    if (sc16) {
+      if (8 * wave < RPC) issue_sc(g, j * RPC + 8 * wave, 8);
+    } else {
+      issue_sc(g, j * RPC + wave * (RPC / 4), RPC / 4);
+    }
+  };
 
   if (tid < 16) {
     const int m = m0 + tid;
@@ -103,156 +165,167 @@ __global__ __launch_bounds__(256, 8) void fc_decode_kernel(FcArgs a) {
   }
   __syncthreads();
 
-  // staging role: row sr, segment ss.  Rows past the expert's token count are
-  // not loaded: their LDS contents only reach MFMA output columns that are
-  // never stored.
+  // activation staging role: row sr, segment ss (rows past the expert's
+  // token count are not loaded; their MFMA columns are never stored)
   const int sr = tid >> 4, ss = tid & 15;
   const int ssrc = s_src[sr];
   const float sinv = 1.0f / s_rs[sr];
   const uint8_t* act = static_cast<const uint8_t*>(a.act);
   const uint8_t* arow_p = act + (size_t)(ssrc >= 0 ? ssrc : 0) * ((size_t)K * ESZ) + ss * SEGB;
   const uint8_t* asf_p = MODE == 2 ? a.act_sf + (size_t)(ssrc >= 0 ? ssrc : 0) * (K >> 5) : nullptr;
-
-  // Weight-scale staging: once per group of SG chunks the workgroup's 128
-  // rows x SG chunks of scale bytes go to LDS.  Thread t loads the chunk
-  // (t % SG) piece of WG-local rows t / SG + (256 / SG) h, h < SG / 2, so the
-  // SG threads of a row read its SG * SCB contiguous bytes.  WG-local rows:
-  // FC1 0..63 gate and 64..127 up of the 64 outputs; FC2 128 consecutive rows.
-  constexpr int NH = SG / 2;  // rows staged per thread
-  const int sq = tid % SG, slr = tid / SG;
-  const uint8_t* sc_src[NH];
-#pragma unroll
-  for (int h = 0; h < NH; ++h) {
-    const int lr = slr + (256 / SG) * h;
-    int grow;
-    if (FC1) {
-      const int i0 = blockIdx.x * 64 + (lr & 63);
-      grow = ((lr >= 64) != (a.w13_order != 0)) ? a.I + i0 : i0;
-    } else {
-      grow = blockIdx.x * 128 + lr;
+  uint4 av0 = {0u, 0u, 0u, 0u}, av1 = {0u, 0u, 0u, 0u};
+  uint2 avs = {0u, 0u};
+  auto load_act = [&](int c) __attribute__((always_inline)) {
+    if (ssrc >= 0) {
+      av0 = *reinterpret_cast<const uint4*>(arow_p + (size_t)c * (KC * ESZ));
+      if (SEGB == 32) av1 = *reinterpret_cast<const uint4*>(arow_p + (size_t)c * (KC * ESZ) + 16);
+      if (MODE == 2 && ss == 0) avs = *reinterpret_cast<const uint2*>(asf_p + c * (KC / 32));
     }
-    sc_src[h] = a.wsf + ((size_t)e * N + grow) * sb + sq * SCB;
-  }
-  // this lane's rows in the staged scales
+  };
+
+  // this lane's weight rows (workgroup-local)
   const int lrow0 = FC1 ? wave * 16 + r16 : wave * 32 + r16;
   const int lrow1 = FC1 ? 64 + wave * 16 + r16 : wave * 32 + 16 + r16;
+  int obase = FC1 ? blockIdx.x * 64 + wave * 16 : blockIdx.x * 128 + wave * 32;
+
+  // the lane's weight-scale bytes of the current group, one entry per chunk
+  // (group16: the 4 scales of K [64 q, 64 q + 64) for each of the two rows;
+  // group32: the 2 scales of each row, row 0 in the low half); consumed
+  // from entry 0 and shifted down each chunk
+  constexpr int NSR = MODE == 0 ? 2 * SG : SG;
+  uint32_t sreg[NSR];
+#pragma unroll
+  for (int i = 0; i < NSR; ++i) sreg[i] = 0;
+
+  // prologue: group 0's scale lines, chunk 0's activations and weights
+  issue_sc(0, 32 * wave, 32);
+  load_act(0);
+  issue_w(0);
 
   v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  const int nchunks = K / KC;
   for (int c = 0; c < nchunks; ++c) {
-    const int k0 = c * KC;
-    // activation segment of this thread
-    uint4 bv0 = {0u, 0u, 0u, 0u}, bv1 = {0u, 0u, 0u, 0u};
-    uint2 bsf = {0u, 0u};
+    // stage chunk c's activations
     if (ssrc >= 0) {
-      bv0 = *reinterpret_cast<const uint4*>(arow_p + (size_t)k0 * ESZ);
-      if (SEGB == 32) bv1 = *reinterpret_cast<const uint4*>(arow_p + (size_t)k0 * ESZ + 16);
-      if (MODE == 2) bsf = *reinterpret_cast<const uint2*>(asf_p + (k0 >> 5));
-    }
-    // weight scales of the next 4 chunks
-    const bool sgroup = (c % SG) == 0;
-    ScPiece sp[NH];
-#pragma unroll
-    for (int h = 0; h < NH; ++h) sp[h] = ScPiece{};
-    if (sgroup && c + sq < nchunks) {
-      const size_t off = (size_t)(k0 / KC) * SCB;
-#pragma unroll
-      for (int h = 0; h < NH; ++h) sp[h] = *reinterpret_cast<const ScPiece*>(sc_src[h] + off);
-    }
-    // weights: pieces i = 0, 1 of 16 bytes at row offset 16 q + 64 i
-    const uint4 c00 = *reinterpret_cast<const uint4*>(wc0 + (k0 >> 1));
-    const uint4 c01 = *reinterpret_cast<const uint4*>(wc0 + (k0 >> 1) + 64);
-    const uint4 c10 = *reinterpret_cast<const uint4*>(wc1 + (k0 >> 1));
-    const uint4 c11 = *reinterpret_cast<const uint4*>(wc1 + (k0 >> 1) + 64);
-    if (MODE == 0) {
-      // bf16 x or h -> fp16 * 2**-p (exact: 8 significant bits, in range)
-      uint32_t w[8] = {bv0.x, bv0.y, bv0.z, bv0.w, bv1.x, bv1.y, bv1.z, bv1.w};
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const _Float16 lo = (_Float16)(bf16_to_f32(w[j] & 0xFFFFu) * sinv);
-        const _Float16 hi = (_Float16)(bf16_to_f32(w[j] >> 16) * sinv);
-        w[j] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-      }
-      bv0 = uint4{w[0], w[1], w[2], w[3]};
-      bv1 = uint4{w[4], w[5], w[6], w[7]};
-    }
-    uint8_t* d = s_b + sr * ROWB + ss * SEGB;
-    *reinterpret_cast<uint4*>(d) = bv0;
-    if (SEGB == 32) *reinterpret_cast<uint4*>(d + 16) = bv1;
-    if (MODE == 2 && ss == 0) *reinterpret_cast<uint2*>(s_bsf + sr * 8) = bsf;
-    if (sgroup) {
-#pragma unroll
-      for (int h = 0; h < NH; ++h)
-        *reinterpret_cast<ScPiece*>(s_sc + (slr + (256 / SG) * h) * SCROW + sq * SCB) = sp[h];
-    }
-    __syncthreads();
-
-    // scales of the two pieces of the two tiles
-    uint32_t s0a, s0b, s1a, s1b;
-    {
-      const uint8_t* p0 = s_sc + lrow0 * SCROW + (c % SG) * SCB;
-      const uint8_t* p1 = s_sc + lrow1 * SCROW + (c % SG) * SCB;
+      uint4 v0 = av0, v1 = av1;
       if (MODE == 0) {
-        // piece i needs the group16 scales 8 i + 2 q and + 1
-        s0a = *reinterpret_cast<const uint16_t*>(p0 + 2 * q);
-        s0b = *reinterpret_cast<const uint16_t*>(p0 + 8 + 2 * q);
-        s1a = *reinterpret_cast<const uint16_t*>(p1 + 2 * q);
-        s1b = *reinterpret_cast<const uint16_t*>(p1 + 8 + 2 * q);
-      } else {
-        // the chunk's 8 UE8M0 bytes (piece / step i uses byte 4 i + q)
-        const uint2 v0 = *reinterpret_cast<const uint2*>(p0);
-        const uint2 v1 = *reinterpret_cast<const uint2*>(p1);
-        s0a = v0.x; s0b = v0.y; s1a = v1.x; s1b = v1.y;
+        // bf16 x or h -> fp16 * 2**-p (exact: 8 significant bits, in range)
+        uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const _Float16 lo = (_Float16)(bf16_to_f32(w[j] & 0xFFFFu) * sinv);
+          const _Float16 hi = (_Float16)(bf16_to_f32(w[j] >> 16) * sinv);
+          w[j] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+        }
+        v0 = uint4{w[0], w[1], w[2], w[3]};
+        v1 = uint4{w[4], w[5], w[6], w[7]};
+      }
+      uint8_t* d = s_b + sr * AROW + ss * SEGB;
+      *reinterpret_cast<uint4*>(d) = v0;
+      if (SEGB == 32) *reinterpret_cast<uint4*>(d + 16) = v1;
+      if (MODE == 2 && ss == 0) *reinterpret_cast<uint2*>(s_bsf + sr * 8) = avs;
+    }
+    __syncthreads();  // also waits for this chunk's weight and scale loads
+
+    // every operand of the chunk into registers
+    const int j = c % SG;
+    if (j == 0) {
+      // a new scale group: this lane's scales of all its chunks
+      const int x0 = 4 * sc_swz(lrow0), x1 = 4 * sc_swz(lrow1);
+      const uint8_t* p0 = s_sc + lrow0 * 128;
+      const uint8_t* p1 = s_sc + lrow1 * 128;
+#pragma unroll
+      for (int jj = 0; jj < SG; ++jj) {
+        if (MODE == 0) {
+          const int d = 4 * jj + q;
+          sreg[2 * jj] = *reinterpret_cast<const uint32_t*>(p0 + 4 * (d ^ x0));
+          sreg[2 * jj + 1] = *reinterpret_cast<const uint32_t*>(p1 + 4 * (d ^ x1));
+        } else {
+          const int d = 2 * jj + (q >> 1), h = 2 * (q & 1);
+          sreg[jj] = (uint32_t)*reinterpret_cast<const uint16_t*>(p0 + 4 * (d ^ x0) + h) |
+                     ((uint32_t)*reinterpret_cast<const uint16_t*>(p1 + 4 * (d ^ x1) + h) << 16);
+        }
       }
     }
-
-    const uint8_t* brow = s_b + r16 * ROWB;
+    const uint32_t s0 = MODE == 0 ? sreg[0] : (sreg[0] & 0xFFFFu);
+    const uint32_t s1 = MODE == 0 ? sreg[1] : (sreg[0] >> 16);
+    constexpr int SSH = MODE == 0 ? 2 : 1;
+#pragma unroll
+    for (int i = 0; i + SSH < NSR; ++i) sreg[i] = sreg[i + SSH];
+    const uint4 w0a = *reinterpret_cast<const uint4*>(s_w + lrow0 * 128 + 16 * ((2 * q) ^ (lrow0 & 7)));
+    const uint4 w0b = *reinterpret_cast<const uint4*>(s_w + lrow0 * 128 + 16 * ((2 * q + 1) ^ (lrow0 & 7)));
+    const uint4 w1a = *reinterpret_cast<const uint4*>(s_w + lrow1 * 128 + 16 * ((2 * q) ^ (lrow1 & 7)));
+    const uint4 w1b = *reinterpret_cast<const uint4*>(s_w + lrow1 * 128 + 16 * ((2 * q + 1) ^ (lrow1 & 7)));
+    const uint8_t* brow = s_b + r16 * AROW;
+    uint4 bv[8];
+    int sbb0 = 0, sbb1 = 0;
     if (MODE == 2) {
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        const uint4 b0 = *reinterpret_cast<const uint4*>(brow + 128 * st + 16 * q);
-        const uint4 b1 = *reinterpret_cast<const uint4*>(brow + 128 * st + 64 + 16 * q);
-        const v8i B = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
-        const int sbb = s_bsf[r16 * 8 + 4 * st + q];
-        const uint4& ca = st ? c01 : c00;
-        const uint4& cb = st ? c11 : c10;
-        const int sa0 = (int)(((st ? s0b : s0a) >> (8 * q)) & 0xFFu);
-        const int sa1 = (int)(((st ? s1b : s1a) >> (8 * q)) & 0xFFu);
-        const v8i A0 = {(int)ca.x, (int)ca.y, (int)ca.z, (int)ca.w, 0, 0, 0, 0};
-        const v8i A1 = {(int)cb.x, (int)cb.y, (int)cb.z, (int)cb.w, 0, 0, 0, 0};
-        acc0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A0, B, acc0, 4, 0, 0, sa0, 0, sbb);
-        acc1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A1, B, acc1, 4, 0, 0, sa1, 0, sbb);
+        const int o = 64 * (q >> 1) + 32 * st + 16 * (q & 1);
+        bv[2 * st] = *reinterpret_cast<const uint4*>(brow + o);
+        bv[2 * st + 1] = *reinterpret_cast<const uint4*>(brow + 128 + o);
       }
+      const uint32_t sbb = *reinterpret_cast<const uint16_t*>(s_bsf + r16 * 8 + 2 * q);
+      sbb0 = (int)(sbb & 0xFFu);
+      sbb1 = (int)(sbb >> 8);
     } else {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const uint4& ca = i ? c01 : c00;
-        const uint4& cb = i ? c11 : c10;
-        v2h sp0, sp1;
-        if (MODE == 0) {
-          sp0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(i ? s0b : s0a, 1.0f, false);
-          sp1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(i ? s1b : s1a, 1.0f, false);
-        }
+      for (int jj = 0; jj < 8; ++jj) bv[jj] = *reinterpret_cast<const uint4*>(brow + 128 * q + 16 * jj);
+    }
+    __syncthreads();  // operands read: the buffers may be refilled
+
+    // next chunk's loads, then this chunk's MFMAs
+    if (c + 1 < nchunks) {
+      load_act(c + 1);
+      issue_w(c + 1);
+    }
+    if (c / SG + 1 < ngroups) issue_sc_slice(c / SG + 1, j);
+
+    if (MODE == 2) {
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const uint4 braw = *reinterpret_cast<const uint4*>(brow + (128 * i + 32 * q + 8 * jj) * 2);
-          if (MODE == 0) {
-            const v2h x0 = jj < 2 ? v2h{sp0[0], sp0[0]} : v2h{sp0[1], sp0[1]};
-            const v2h x1 = jj < 2 ? v2h{sp1[0], sp1[0]} : v2h{sp1[1], sp1[1]};
-            const v8h B = __builtin_bit_cast(v8h, braw);
-            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(dq8_f16(dw(ca, jj), x0), B, acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(dq8_f16(dw(cb, jj), x1), B, acc1, 0, 0, 0);
-          } else {
-            const float x0 = ue8m0_to_f32(((i ? s0b : s0a) >> (8 * q)) & 0xFFu);
-            const float x1 = ue8m0_to_f32(((i ? s1b : s1a) >> (8 * q)) & 0xFFu);
-            const v8bf B = __builtin_bit_cast(v8bf, braw);
-            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dq8_bf16(dw(ca, jj), x0), B, acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dq8_bf16(dw(cb, jj), x1), B, acc1, 0, 0, 0);
-          }
-        }
+      for (int st = 0; st < 2; ++st) {
+        const uint4& ca = st ? w0b : w0a;
+        const uint4& cb = st ? w1b : w1a;
+        const v8i B = {(int)bv[2 * st].x, (int)bv[2 * st].y, (int)bv[2 * st].z, (int)bv[2 * st].w,
+                       (int)bv[2 * st + 1].x, (int)bv[2 * st + 1].y, (int)bv[2 * st + 1].z,
+                       (int)bv[2 * st + 1].w};
+        const v8i A0 = {(int)ca.x, (int)ca.y, (int)ca.z, (int)ca.w, 0, 0, 0, 0};
+        const v8i A1 = {(int)cb.x, (int)cb.y, (int)cb.z, (int)cb.w, 0, 0, 0, 0};
+        const int sa0 = (int)((s0 >> (8 * st)) & 0xFFu);
+        const int sa1 = (int)((s1 >> (8 * st)) & 0xFFu);
+        const int sbv = st ? sbb1 : sbb0;
+        acc0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A0, B, acc0, 4, 0, 0, sa0, 0, sbv);
+        acc1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A1, B, acc1, 4, 0, 0, sa1, 0, sbv);
+      }
+    } else if (MODE == 0) {
+      // group16 scale of MFMA j: byte j / 2 of s0 / s1
+      const v2h p0l = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s0, 1.0f, false);
+      const v2h p0h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s0, 1.0f, true);
+      const v2h p1l = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s1, 1.0f, false);
+      const v2h p1h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s1, 1.0f, true);
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const _Float16 h0 = jj < 2 ? p0l[0] : jj < 4 ? p0l[1] : jj < 6 ? p0h[0] : p0h[1];
+        const _Float16 h1 = jj < 2 ? p1l[0] : jj < 4 ? p1l[1] : jj < 6 ? p1h[0] : p1h[1];
+        const uint32_t c0 = jj < 4 ? dw(w0a, jj) : dw(w0b, jj - 4);
+        const uint32_t c1 = jj < 4 ? dw(w1a, jj) : dw(w1b, jj - 4);
+        const v8h B = __builtin_bit_cast(v8h, bv[jj]);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(dq8_f16(c0, v2h{h0, h0}), B, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(dq8_f16(c1, v2h{h1, h1}), B, acc1, 0, 0, 0);
+      }
+    } else {
+      // group32 scale of MFMA j: byte j / 4 of s0 / s1
+      const float x0l = ue8m0_to_f32(s0 & 0xFFu), x0h = ue8m0_to_f32(s0 >> 8);
+      const float x1l = ue8m0_to_f32(s1 & 0xFFu), x1h = ue8m0_to_f32(s1 >> 8);
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const uint32_t c0 = jj < 4 ? dw(w0a, jj) : dw(w0b, jj - 4);
+        const uint32_t c1 = jj < 4 ? dw(w1a, jj) : dw(w1b, jj - 4);
+        const v8bf B = __builtin_bit_cast(v8bf, bv[jj]);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dq8_bf16(c0, jj < 4 ? x0l : x0h), B, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dq8_bf16(c1, jj < 4 ? x1l : x1h), B, acc1, 0, 0, 0);
       }
     }
-    __syncthreads();
   }
 
   // epilogue: lane holds rows 4q..4q+3 of each 16-row tile, column r16
