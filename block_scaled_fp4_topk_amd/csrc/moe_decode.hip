@@ -24,9 +24,10 @@
 // group16 weights, exact).
 //
 // Per chunk: stage the activations, barrier, read every operand of the
-// chunk into registers, barrier, issue the next chunk's loads, MFMAs.  Three
-// workgroups per CU (41 KB of LDS each) keep loads in flight while others
-// read and compute.
+// chunk into registers, issue the next chunk's loads (into a second set of
+// buffers, or into the same ones after a second barrier), MFMAs.  Two or
+// three workgroups per CU keep loads in flight while others read and
+// compute.
 //
 // K index permutation inside a chunk (identical for both MFMA operands):
 // lane group q (= lane / 16) holds code bytes [32 q, 32 q + 32) of a row,
@@ -57,18 +58,32 @@ __device__ __forceinline__ uint32_t dw(const uint4& v, int r) {
 // consecutive rows hit 16 distinct bank groups
 __device__ __forceinline__ int sc_swz(int lr) { return (lr >> 1) & 7; }
 
+// RING2: chunk buffers in pairs, so the next chunk's loads are issued right
+// after the chunk's barrier (two workgroups per CU, one barrier per chunk);
+// otherwise one set of buffers, refilled after a second barrier once every
+// wave has read its operands (three workgroups per CU).  Measured per kernel
+// on the decode16 geometry: the pair wins only where the MFMA phase is
+// longest (group16 FC1, 512 vs 545 us); elsewhere the extra workgroup per
+// CU wins (e.g. group16 FC2 268 vs 277 us, FP8 FC1 471 vs 486 us).
 template <int MODE, bool FC1>
-__global__ __launch_bounds__(256, 3) void fc_decode_kernel(FcArgs a) {
+__global__ __launch_bounds__(256, (MODE == 0 && FC1) ? 2 : 3) void fc_decode_kernel(FcArgs a) {
+  constexpr bool RING2 = MODE == 0 && FC1;
   constexpr int ESZ = MODE == 2 ? 1 : 2;               // activation element bytes
   constexpr int AROW = KC * ESZ + 16;                  // staged activation row stride
   constexpr int SEGB = KC * ESZ / 16;                  // activation bytes per thread (32 or 16)
   constexpr int SCB = MODE == 0 ? KC / 16 : KC / 32;   // weight-scale bytes per row per chunk
   constexpr int SG = 128 / SCB;                        // chunks per scale group
   constexpr int RPC = WR / SG;                         // scale lines staged per chunk (16 or 8)
-  __shared__ __attribute__((aligned(16))) uint8_t s_w[WR * 128];
+  // RING2 pairs (even / odd chunks) are distinct arrays, so the loads into
+  // one never make the compiler wait before reading the other
+  constexpr int NB1 = RING2 ? 1 : 0;
+  __shared__ __attribute__((aligned(16))) uint8_t s_w0[WR * 128];
+  __shared__ __attribute__((aligned(16))) uint8_t s_w1[NB1 * WR * 128 + 16];
   __shared__ __attribute__((aligned(16))) uint8_t s_sc[WR * 128];
-  __shared__ __attribute__((aligned(16))) uint8_t s_b[16 * AROW];
-  __shared__ __attribute__((aligned(16))) uint8_t s_bsf[16 * 8];
+  __shared__ __attribute__((aligned(16))) uint8_t s_b0[16 * AROW];
+  __shared__ __attribute__((aligned(16))) uint8_t s_b1[NB1 * 16 * AROW + 16];
+  __shared__ __attribute__((aligned(16))) uint8_t s_bsf0[16 * 8];
+  __shared__ __attribute__((aligned(16))) uint8_t s_bsf1[NB1 * 16 * 8 + 16];
   __shared__ int s_src[16];
   __shared__ float s_rs[16];
   __shared__ float s_amax[4][16];
@@ -106,11 +121,10 @@ __global__ __launch_bounds__(256, 3) void fc_decode_kernel(FcArgs a) {
     const int lr = 32 * wave + 8 * i + (lane >> 3);
     wsrc[i] = wexp + (size_t)wrow(lr) * rowb + 16 * ((lane & 7) ^ (lr & 7));
   }
-  auto issue_w = [&](int c) __attribute__((always_inline)) {
+  auto issue_w = [&](int c, uint8_t* sw) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_global_load_lds(wsrc[i] + (size_t)c * 128, &s_w[(32 * wave + 8 * i) * 128], 16, 0,
-                                       kNT);
+      __builtin_amdgcn_global_load_lds(wsrc[i] + (size_t)c * 128, sw + (32 * wave + 8 * i) * 128, 16, 0, kNT);
   };
   // scale loads: this wave's rows [rb0, rb0 + nrows) of group g's 128-byte
   // lines, 16 bytes per lane (8 rows per instruction) when the scale rows
@@ -134,8 +148,8 @@ __global__ __launch_bounds__(256, 3) void fc_decode_kernel(FcArgs a) {
       }
     }
   };
-  // the slice of group g's lines staged while chunk j (0..SG-1) of the group
-  // before it runs: rows [j RPC, (j + 1) RPC), split over the waves
+  // slice j (0..SG-1) of group g's lines: rows [j RPC, (j + 1) RPC), split
+  // over the waves
   auto issue_sc_slice = [&](int g, int j) __attribute__((always_inline)) {
     if (sc16) {
       if (8 * wave < RPC) issue_sc(g, j * RPC + 8 * wave, 8);
@@ -200,10 +214,14 @@ __global__ __launch_bounds__(256, 3) void fc_decode_kernel(FcArgs a) {
   // prologue: group 0's scale lines, chunk 0's activations and weights
   issue_sc(0, 32 * wave, 32);
   load_act(0);
-  issue_w(0);
+  issue_w(0, s_w0);
 
   v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  for (int c = 0; c < nchunks; ++c) {
+  // one chunk: its weights (sw) and activations (sb, sbsf) were loaded
+  // during the previous chunk; RING2 loads the next chunk into the other
+  // buffers (sw_next)
+  auto step = [&](int c, const uint8_t* sw, uint8_t* sw_next, uint8_t* sb, uint8_t* sbsf)
+      __attribute__((always_inline)) {
     // stage chunk c's activations
     if (ssrc >= 0) {
       uint4 v0 = av0, v1 = av1;
@@ -219,14 +237,16 @@ __global__ __launch_bounds__(256, 3) void fc_decode_kernel(FcArgs a) {
         v0 = uint4{w[0], w[1], w[2], w[3]};
         v1 = uint4{w[4], w[5], w[6], w[7]};
       }
-      uint8_t* d = s_b + sr * AROW + ss * SEGB;
+      uint8_t* d = sb + sr * AROW + ss * SEGB;
       *reinterpret_cast<uint4*>(d) = v0;
       if (SEGB == 32) *reinterpret_cast<uint4*>(d + 16) = v1;
-      if (MODE == 2 && ss == 0) *reinterpret_cast<uint2*>(s_bsf + sr * 8) = avs;
+      if (MODE == 2 && ss == 0) *reinterpret_cast<uint2*>(sbsf + sr * 8) = avs;
     }
-    __syncthreads();  // also waits for this chunk's weight and scale loads
+    // also waits for this chunk's weight and scale loads; every wave is past
+    // the previous chunk, so the other buffers and the scale lines read at
+    // the last group start may be refilled
+    __syncthreads();
 
-    // every operand of the chunk into registers
     const int j = c % SG;
     if (j == 0) {
       // a new scale group: this lane's scales of all its chunks
@@ -251,11 +271,28 @@ __global__ __launch_bounds__(256, 3) void fc_decode_kernel(FcArgs a) {
     constexpr int SSH = MODE == 0 ? 2 : 1;
 #pragma unroll
     for (int i = 0; i + SSH < NSR; ++i) sreg[i] = sreg[i + SSH];
-    const uint4 w0a = *reinterpret_cast<const uint4*>(s_w + lrow0 * 128 + 16 * ((2 * q) ^ (lrow0 & 7)));
-    const uint4 w0b = *reinterpret_cast<const uint4*>(s_w + lrow0 * 128 + 16 * ((2 * q + 1) ^ (lrow0 & 7)));
-    const uint4 w1a = *reinterpret_cast<const uint4*>(s_w + lrow1 * 128 + 16 * ((2 * q) ^ (lrow1 & 7)));
-    const uint4 w1b = *reinterpret_cast<const uint4*>(s_w + lrow1 * 128 + 16 * ((2 * q + 1) ^ (lrow1 & 7)));
-    const uint8_t* brow = s_b + r16 * AROW;
+
+    // RING2: the next chunk's loads now.  The next group's scale lines
+    // arrive a slice per chunk from the group's second chunk on (the group
+    // start above has just read the buffer; every wave is past it one
+    // barrier later), the last chunk of the group taking the last two slices.
+    if (RING2) {
+      if (c + 1 < nchunks) {
+        load_act(c + 1);
+        issue_w(c + 1, sw_next);
+      }
+      if (c / SG + 1 < ngroups && j > 0) {
+        issue_sc_slice(c / SG + 1, j - 1);
+        if (j == SG - 1) issue_sc_slice(c / SG + 1, SG - 1);
+      }
+    }
+
+    // this chunk's operands, then its MFMAs
+    const uint4 w0a = *reinterpret_cast<const uint4*>(sw + lrow0 * 128 + 16 * ((2 * q) ^ (lrow0 & 7)));
+    const uint4 w0b = *reinterpret_cast<const uint4*>(sw + lrow0 * 128 + 16 * ((2 * q + 1) ^ (lrow0 & 7)));
+    const uint4 w1a = *reinterpret_cast<const uint4*>(sw + lrow1 * 128 + 16 * ((2 * q) ^ (lrow1 & 7)));
+    const uint4 w1b = *reinterpret_cast<const uint4*>(sw + lrow1 * 128 + 16 * ((2 * q + 1) ^ (lrow1 & 7)));
+    const uint8_t* brow = sb + r16 * AROW;
     uint4 bv[8];
     int sbb0 = 0, sbb1 = 0;
     if (MODE == 2) {
@@ -265,22 +302,21 @@ __global__ __launch_bounds__(256, 3) void fc_decode_kernel(FcArgs a) {
         bv[2 * st] = *reinterpret_cast<const uint4*>(brow + o);
         bv[2 * st + 1] = *reinterpret_cast<const uint4*>(brow + 128 + o);
       }
-      const uint32_t sbb = *reinterpret_cast<const uint16_t*>(s_bsf + r16 * 8 + 2 * q);
+      const uint32_t sbb = *reinterpret_cast<const uint16_t*>(sbsf + r16 * 8 + 2 * q);
       sbb0 = (int)(sbb & 0xFFu);
       sbb1 = (int)(sbb >> 8);
     } else {
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) bv[jj] = *reinterpret_cast<const uint4*>(brow + 128 * q + 16 * jj);
     }
-    __syncthreads();  // operands read: the buffers may be refilled
-
-    // next chunk's loads, then this chunk's MFMAs
-    if (c + 1 < nchunks) {
-      load_act(c + 1);
-      issue_w(c + 1);
+    if (!RING2) {
+      __syncthreads();  // operands read: the buffers may be refilled
+      if (c + 1 < nchunks) {
+        load_act(c + 1);
+        issue_w(c + 1, s_w0);
+      }
+      if (c / SG + 1 < ngroups) issue_sc_slice(c / SG + 1, j);
     }
-    if (c / SG + 1 < ngroups) issue_sc_slice(c / SG + 1, j);
-
     if (MODE == 2) {
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
@@ -326,6 +362,14 @@ __global__ __launch_bounds__(256, 3) void fc_decode_kernel(FcArgs a) {
         acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dq8_bf16(c1, jj < 4 ? x1l : x1h), B, acc1, 0, 0, 0);
       }
     }
+  };
+  if (RING2) {
+    for (int c = 0; c < nchunks; c += 2) {
+      step(c, s_w0, s_w1, s_b0, s_bsf0);
+      if (c + 1 < nchunks) step(c + 1, s_w1, s_w0, s_b1, s_bsf1);
+    }
+  } else {
+    for (int c = 0; c < nchunks; ++c) step(c, s_w0, s_w0, s_b0, s_bsf0);
   }
 
   // epilogue: lane holds rows 4q..4q+3 of each 16-row tile, column r16
