@@ -48,6 +48,14 @@ SMALL = (combos(synth.CONFIGS["tiny"])
                                 routing="zipf")))
 
 
+# decode regime (16-row tiles) with long K: several scale groups per row, a
+# one-chunk last group (FC1 group16: 17 chunks = 8 + 8 + 1; FC2 group16: 9
+# = 8 + 1), and scale rows that are not 16-byte multiples (group32: 136 and
+# 72 bytes)
+DECODE_LONG_K = combos(synth.variant(synth.CONFIGS["tiny"], T=16, E=8, k=4, H=4352, I=2304, seed=25))
+SMALL = SMALL + DECODE_LONG_K
+
+
 @pytest.mark.parametrize("cfg", SMALL, ids=[_id(c) for c in SMALL])
 def test_forward_small(cfg):
     require_gpu()
