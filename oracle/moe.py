@@ -71,7 +71,10 @@ def route(topk_ids, E: int):
 
 def silu(z):
     z = np.asarray(z, dtype=np.float64)
-    return z / (1.0 + np.exp(-z))
+    # exp(-z) overflows to inf for z < -709; z / inf is then the exact
+    # limit (-0.0), so the overflow is expected and not reported
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
 
 
 def quantize_h_a8(h):
