@@ -35,4 +35,4 @@ from .formats import (  # noqa: F401
     dequant_fp4,
 )
 from .requant import requant_g16_to_g32, requant_block  # noqa: F401
-from .moe import route, moe_forward, quantize_h_a8, silu, h_decision_band  # noqa: F401
+from .moe import route, moe_forward, quantize_h_a8, quantize_a4, silu, h_decision_band  # noqa: F401

@@ -17,6 +17,13 @@ with K/16 E4M3 or K/32 E8M0 scales):
   h quant  A16: RNE to bfloat16 (one rounding from FP64);
            A8 : per assignment, per 32 consecutive I elements, UE8M0 exponent
                 e = ceil(log2(amax / 448)) and E4M3 RNE of h / 2**e;
+           A4 : per assignment, per 32 consecutive I elements, the block rule
+                of the group32 requantisation ([P1] ``requant_fp4_to_gran_k``,
+                [P2] "Requantization path"): UE8M0 e = ceil(log2(amax / 6))
+                and E2M1 RNE of h / 2**e (the activations x arrive in the same
+                MXFP4 form: "A4 prefill" of [P3] ``prepare_w4a16_modelopt_-
+                native_weights``, read as the block-scaled FP4 format the
+                matrix instruction consumes);
   FC2      Y[a, :] = sum_i hhat[a, i] * W2_e[:, i];
   combine  out[t] = sum_j topk_w[t, j] * Y[slot_of[t*k + j]], j ascending.
 
@@ -32,12 +39,16 @@ import numpy as np
 from .formats import (
     bf16_bits_decode,
     dequant_fp4,
+    e2m1_decode,
     e4m3_decode,
+    pack_fp4,
     rne_bf16,
+    rne_e2m1_magnitude,
     rne_e4m3,
     ue8m0_decode,
+    unpack_fp4,
 )
-from .requant import _ceil_log2_ratio
+from .requant import _ceil_log2_ratio, requant_block
 
 
 def route(topk_ids, E: int):
@@ -94,6 +105,22 @@ def quantize_h_a8(h):
     return hhat.reshape(n, I), q.reshape(n, I), (e + 127).astype(np.uint8)
 
 
+def quantize_a4(v):
+    """MXFP4 rows: per row, per 32 consecutive elements, the requantisation
+    block rule (UE8M0 e = ceil(log2(amax / 6)), amax == 0 -> e = -127, E2M1
+    RNE of v / 2**e with the sign kept).  Returns (vhat values FP64, packed
+    codes [n, K/2] uint8 with element 2j in the low nibble of byte j, scale
+    bytes [n, K/32])."""
+    v = np.asarray(v, dtype=np.float64)
+    n, K = v.shape
+    codes, sb = requant_block(v.reshape(n, K // 32, 32))
+    vhat = e2m1_decode(codes) * np.ldexp(1.0, sb.astype(np.int64) - 127)[..., None]
+    return vhat.reshape(n, K), pack_fp4(codes.reshape(n, K)), sb
+
+
+E2M1_POS = e2m1_decode(np.arange(8, dtype=np.uint8))  # magnitudes of codes 0..7
+
+
 # A rounding decision of h is taken as undecided between its two
 # neighbouring results when h lies within DECISION_RADIUS * (max |h| of its
 # 32-element block) of the decision boundary.  An FP32-accumulated h (the
@@ -116,53 +143,69 @@ def _grid_ambiguity(y, mant_bits, emin, radius):
     return np.where(near, quantum, 0.0)
 
 
-def h_decision_band(h, a8, radius=DECISION_RADIUS):
+def h_decision_band(h, a8, radius=DECISION_RADIUS, a4=False):
     """Per element, the largest change of the quantised h that a rounding
     decision within ``radius`` * (block max |h|) could make: one grid step
-    where h is that close to a rounding midpoint and, for A8, the whole
+    where h is that close to a rounding midpoint and, for A8 / A4, the whole
     requantisation of a 32-block under the neighbouring exponent where amax
-    is that close to 448 * 2**e.  Zero where every decision is clear."""
+    is that close to 448 * 2**e (6 * 2**e).  Zero where every decision is
+    clear."""
     h = np.asarray(h, dtype=np.float64)
     n, I = h.shape
     blk = h.reshape(n, I // 32, 32)
     amax = np.max(np.abs(blk), axis=-1)
     rad = radius * amax[..., None]
-    if not a8:
+    if not a8 and not a4:
         return _grid_ambiguity(blk, 7, -126, rad).reshape(n, I)
-    hhat, _, sb = quantize_h_a8(h)
+    if a4:
+        hhat, _, sb = quantize_a4(h)
+        top, mant, emin = 6.0, 1, 0
+
+        def requant_at(e2):
+            y = np.clip(np.ldexp(np.abs(blk), -e2[..., None]), 0, 6)
+            return np.copysign(E2M1_POS[rne_e2m1_magnitude(y)], blk) * np.ldexp(1.0, e2[..., None])
+    else:
+        hhat, _, sb = quantize_h_a8(h)
+        top, mant, emin = 448.0, 3, -6
+
+        def requant_at(e2):
+            return np.ldexp(e4m3_decode(rne_e4m3(np.clip(np.ldexp(blk, -e2[..., None]), -448, 448))),
+                            e2[..., None])
     hhat = hhat.reshape(n, I // 32, 32)
     e = sb.astype(np.int64) - 127
-    band = _grid_ambiguity(np.ldexp(blk, -e[..., None]), 3, -6,
+    band = _grid_ambiguity(np.ldexp(blk, -e[..., None]), mant, emin,
                            np.ldexp(rad, -e[..., None])) * np.ldexp(1.0, e[..., None])
     for de in (-1, 1):
         e2 = e + de
-        lim = np.ldexp(448.0, np.minimum(e, e2))  # the boundary between e and e2
+        lim = np.ldexp(top, np.minimum(e, e2))  # the boundary between e and e2
         close = (amax > 0) & (np.abs(amax - lim) <= radius * amax)
         if np.any(close):
-            alt = np.ldexp(e4m3_decode(rne_e4m3(np.clip(np.ldexp(blk, -e2[..., None]), -448, 448))),
-                           e2[..., None])
+            alt = requant_at(e2)
             band = np.where(close[..., None], np.maximum(band, np.abs(alt - hhat)), band)
     return band.reshape(n, I)
 
 
-def decode_activations(x, x_sf=None):
+def decode_activations(x, x_sf=None, a4=False):
     """A16: x is [T, H] bfloat16 bit patterns (uint16).  A8: x is [T, H]
-    E4M3 bytes and x_sf [T, H/32] UE8M0 bytes; value = fp8 * 2**(sf - 127)."""
+    E4M3 bytes and x_sf [T, H/32] UE8M0 bytes; value = fp8 * 2**(sf - 127).
+    A4: x is [T, H/2] packed E2M1 codes (element 2j in the low nibble of byte
+    j) and x_sf [T, H/32] UE8M0 bytes; value = e2m1 * 2**(sf - 127)."""
     if x_sf is None:
         return bf16_bits_decode(x)
-    xv = e4m3_decode(x)
+    xv = e2m1_decode(unpack_fp4(x)) if a4 else e4m3_decode(x)
     return xv * np.repeat(ue8m0_decode(x_sf), 32, axis=1)
 
 
 def moe_forward(x, topk_ids, topk_w, w13, w13_sf, w13_gs, w2, w2_sf, w2_gs,
                 gran: int, x_sf=None, w13_order: str = "gate_up",
-                tokens=None, out_cols=None, return_parts=False, return_band=False):
+                tokens=None, out_cols=None, return_parts=False, return_band=False, a4=False):
     """FP64 MoE forward.  Shapes: x [T, H] (see decode_activations),
     topk_ids/topk_w [T, k], w13 [E, 2I, H/2], w13_sf [E, 2I, H/gran],
     w2 [E, H, I/2], w2_sf [E, H, I/gran], gs [E] float32 or None.
 
     gran 16 -> E4M3 block scales, gran 32 -> UE8M0 block scales.
     x_sf given -> A8 activations, and h is quantised to FP8 + UE8M0 per 32;
+    with a4=True as well -> A4 (MXFP4 x, h quantised to E2M1 + UE8M0 per 32);
     otherwise A16 (bfloat16 x, bfloat16 h).
 
     ``tokens`` / ``out_cols`` restrict the computation to a subset of output
@@ -181,12 +224,14 @@ def moe_forward(x, topk_ids, topk_w, w13, w13_sf, w13_gs, w2, w2_sf, w2_gs,
     I = two_i // 2
     H = np.asarray(w2).shape[1]
     kind = {16: "e4m3", 32: "ue8m0"}[gran]
-    a8 = x_sf is not None
+    if a4 and x_sf is None:
+        raise ValueError("A4 activations need x_sf")
+    a8 = x_sf is not None and not a4
     tokens = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
     out_cols = np.arange(H) if out_cols is None else np.asarray(out_cols, dtype=np.int64)
 
     counts, offsets, sorted_assign, slot_of = route(ids, E)
-    xv = decode_activations(x, x_sf)
+    xv = decode_activations(x, x_sf, a4)
     want = np.zeros(T * k, dtype=bool)
     for t in tokens:
         want[t * k:(t + 1) * k] = True
@@ -211,12 +256,12 @@ def moe_forward(x, topk_ids, topk_w, w13, w13_sf, w13_gs, w2, w2_sf, w2_gs,
         else:
             raise ValueError(w13_order)
         h = silu(gate) * up
-        hhat = quantize_h_a8(h)[0] if a8 else rne_bf16(h)
+        hhat = quantize_a4(h)[0] if a4 else quantize_h_a8(h)[0] if a8 else rne_bf16(h)
         W2 = dequant_fp4(np.asarray(w2[e])[out_cols], np.asarray(w2_sf[e])[out_cols],
                          gran, kind, gs2)
         Ye = hhat @ W2.T
         if return_band:
-            YBe = h_decision_band(h, a8) @ np.abs(W2).T
+            YBe = h_decision_band(h, a8, a4=a4) @ np.abs(W2).T
         for r, a in enumerate(assigns):
             Y[int(slot_of[a])] = Ye[r]
             if return_band:
