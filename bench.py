@@ -38,8 +38,11 @@ WORKLOAD_TEXT = {
     "prefill32": "prefill: T=8192 E=256 top-8 Zipf(1.1) H=6144 I=2048, E4M3+UE8M0 k32 x, E2M1 + UE8M0 k32",
     "prefill32_bf16q": "prefill: T=8192 E=256 top-8 Zipf(1.1) H=6144 I=2048, bf16 x quantised by the "
                        "library to E4M3+UE8M0 k32, E2M1 + UE8M0 k32",
+    "prefill32_a4": "A4 prefill: T=8192 E=256 top-8 Zipf(1.1) H=6144 I=2048, bf16 x quantised by the "
+                    "library to MXFP4 (E2M1+UE8M0 k32), h MXFP4, E2M1 + UE8M0 k32 weights",
 }
-DTYPE = {"decode16": "f16", "decode32": "fp8xfp4", "prefill32": "fp8xfp4"}
+DTYPE = {"decode16": "f16", "decode32": "fp8xfp4", "prefill32": "fp8xfp4", "prefill32_bf16q": "fp8xfp4",
+         "prefill32_a4": "fp4xfp4"}
 STAGES = ["route", "act_prep", "fc1_swiglu", "fc2", "combine"]
 
 
@@ -89,12 +92,13 @@ def gpu_forward_into(moe, torch, inp, d, ws, out):
         c = inp.cfg
         p = moe.make_problem(c.T, c.E, c.k, c.H, c.I, c.gran,
                              {"fp8": moe.ACT_FP8_UE8M0_K32,
-                              "bf16q": moe.ACT_BF16_QUANT_FP8_K32}.get(c.act, moe.ACT_BF16))
+                              "bf16q": moe.ACT_BF16_QUANT_FP8_K32,
+                              "bf16q4": moe.ACT_BF16_QUANT_FP4_K32}.get(c.act, moe.ACT_BF16))
         ws = torch.empty(moe.workspace_bytes(p), dtype=torch.uint8, device="cuda")
         out = torch.empty((c.T, c.H), dtype=torch.bfloat16, device="cuda")
     moe.forward(d["x"], d["topk_ids"], d["topk_w"], d["w13"], d["w13_sf"], d["w13_gs"], d["w2"],
                 d["w2_sf"], d["w2_gs"], inp.cfg.gran, x_sf=d["x_sf"], out=out, workspace=ws,
-                quantize_x=inp.cfg.act == "bf16q")
+                quantize_x={"bf16q": "fp8", "bf16q4": "fp4"}.get(inp.cfg.act, False))
     return ws, out
 
 
@@ -105,16 +109,27 @@ def stage_kernel(cfg, ids, stage):
     FP8 x FP4 GEMM or 64-row tiles)."""
     A = ids.size
     active = len(np.unique(ids[ids >= 0]))
-    mode = 2 if cfg.act in ("fp8", "bf16q") else (0 if cfg.gran == 16 else 1)
+    a4 = cfg.act == "bf16q4"
+    mode = 2 if cfg.act in ("fp8", "bf16q", "bf16q4") else (0 if cfg.gran == 16 else 1)
     gemm_ok = (mode == 2 and cfg.I % 512 == 0 and cfg.H % 512 == 0 and cfg.T * cfg.H < 2**31
                and A * cfg.I < 2**31 and cfg.I * cfg.H < 2**31)
-    nt = (8 if gemm_ok else 4) if active and A / active > 16 else 1
+    nt = 8 if a4 else (8 if gemm_ok else 4) if active and A / active > 16 else 1
     if nt == 8:
-        return f"fc_gemm_a8_kernel<{'true' if stage == 'fc1_swiglu' else 'false'}>"
+        return (f"fc_gemm_a8_kernel<{'true' if stage == 'fc1_swiglu' else 'false'}, "
+                f"{'true' if a4 else 'false'}>")
     if nt == 1:
         return f"fc_decode_kernel<{mode}, {'true' if stage == 'fc1_swiglu' else 'false'}>"
     fc1 = "true" if stage == "fc1_swiglu" else "false"
     return f"fc_a8_kernel<{nt}, {fc1}>" if mode == 2 else f"fc_a16_kernel<{cfg.gran}, {nt}, {fc1}>"
+
+
+def workload_cfg(synth, name):
+    """Synthetic configuration of a named workload (the prefill variants
+    take bfloat16 x that the library quantises)."""
+    if name in synth.CONFIGS:
+        return synth.CONFIGS[name]
+    return synth.variant(synth.CONFIGS["prefill32"], name=name,
+                         act="bf16q4" if name.endswith("_a4") else "bf16q")
 
 
 def kernel_file_key(symbol):
@@ -138,6 +153,8 @@ def algorithmic_bytes(cfg, ids):
         x_bytes, h_bytes = T * H * 2, A * I * 2
     elif cfg.act == "bf16q":
         x_bytes, h_bytes = T * H * 2, A * I + A * I // 32
+    elif cfg.act == "bf16q4":
+        x_bytes, h_bytes = T * H * 2, A * I // 2 + A * I // 32
     else:
         x_bytes, h_bytes = T * H + T * H // 32, A * I + A * I // 32
     whole = active * (w13 + w2) + x_bytes + T * H * 2 + T * k * 8
@@ -248,7 +265,7 @@ def main():
         sys.exit(1)
     moe.lib()  # fails loudly if the HIP library is not built
 
-    cfg = synth.CONFIGS[args.workload]
+    cfg = workload_cfg(synth, args.workload)
     print(f"[bench] generating {cfg.name} inputs", file=sys.stderr, flush=True)
     inp = synth.make_moe_inputs(cfg)
     d = to_dev(torch, inp)
@@ -344,9 +361,8 @@ def secondary(moe, torch, synth, args, inp16, d16):
                             "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
     del src13, sf13, gs13, src2, sf2, gs2, d13, s13, d2, s2
     torch.cuda.empty_cache()
-    for name in ("decode32", "prefill32", "prefill32_bf16q"):
-        cfg = (synth.CONFIGS[name] if name in synth.CONFIGS
-               else synth.variant(synth.CONFIGS["prefill32"], name=name, act="bf16q"))
+    for name in ("decode32", "prefill32", "prefill32_bf16q", "prefill32_a4"):
+        cfg = workload_cfg(synth, name)
         print(f"[bench] secondary {name}", file=sys.stderr, flush=True)
         inp = synth.make_moe_inputs(cfg)
         d = to_dev(torch, inp)
@@ -357,7 +373,10 @@ def secondary(moe, torch, synth, args, inp16, d16):
              "stage_ms": stage_ms, "algorithmic_bytes": ab["whole"],
              "hbm_frac": ab["whole"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
              "tflops": flops(cfg) / (ms_step * 1e-3) / 1e12}
-        r["mfma_frac_fp8_peak"] = r["tflops"] / PEAK_TFLOPS["fp8"]
+        if cfg.act == "bf16q4":
+            r["mfma_frac_fp4_peak"] = r["tflops"] / PEAK_TFLOPS["fp4"]
+        else:
+            r["mfma_frac_fp8_peak"] = r["tflops"] / PEAK_TFLOPS["fp8"]
         out[name] = r
         del d
         torch.cuda.empty_cache()

@@ -11,6 +11,8 @@ Functions mirror the C entry points:
   route(problem, topk_ids, ...)       -> moe_fp4_route
   forward(x, topk_ids, topk_w, ...)   -> moe_fp4_forward
   requant_gran_k(src, src_sf, ...)    -> fp4_requant_gran_k
+  quantize_act(x, ...)                -> moe_fp4_quantize_act
+  quantize_act_fp4(x, ...)            -> moe_fp4_quantize_act_fp4
 """
 
 from __future__ import annotations
@@ -19,12 +21,12 @@ import ctypes
 import os
 
 __all__ = ["Problem", "MoeFp4Error", "lib", "workspace_bytes", "route", "forward",
-           "requant_gran_k", "quantize_act", "dropped_assignments", "LIB_PATH"]
+           "requant_gran_k", "quantize_act", "quantize_act_fp4", "dropped_assignments", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoefp4.so")
 
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = range(5)
-ACT_BF16, ACT_FP8_UE8M0_K32, ACT_BF16_QUANT_FP8_K32 = 0, 1, 2
+ACT_BF16, ACT_FP8_UE8M0_K32, ACT_BF16_QUANT_FP8_K32, ACT_FP4_UE8M0_K32, ACT_BF16_QUANT_FP4_K32 = range(5)
 GATE_UP, UP_GATE = 0, 1
 
 
@@ -66,6 +68,8 @@ def lib():
         L.fp4_requant_gran_k.restype = st
         L.moe_fp4_quantize_act.argtypes = [ctypes.c_int64, ctypes.c_int64, _P, _P, _P, _P]
         L.moe_fp4_quantize_act.restype = st
+        L.moe_fp4_quantize_act_fp4.argtypes = [ctypes.c_int64, ctypes.c_int64, _P, _P, _P, _P]
+        L.moe_fp4_quantize_act_fp4.restype = st
         L.moefp4_last_error.argtypes = []
         L.moefp4_last_error.restype = ctypes.c_char_p
         L.moefp4_set_stage_events.argtypes = [_P, ctypes.c_int32]
@@ -144,14 +148,19 @@ def route(problem: Problem, topk_ids, workspace=None, stream=None):
 def forward(x, topk_ids, topk_w, w13, w13_sf, w13_gs, w2, w2_sf, w2_gs, gran_k, x_sf=None,
             w13_order="gate_up", out=None, workspace=None, stream=None, out_dtype=None,
             quantize_x=False):
-    """MoE forward on the GPU.  x: [T, H] bfloat16 (A16) or uint8/float8_e4m3fn
-    with x_sf [T, H/32] uint8 (A8); quantize_x=True with bfloat16 x asks the
-    library to quantise x to the A8 format first (act_fmt BF16_QUANT_FP8_K32).
+    """MoE forward on the GPU.  x: [T, H] bfloat16 (A16); uint8/float8_e4m3fn
+    [T, H] with x_sf [T, H/32] uint8 (A8); or uint8 [T, H/2] (two E2M1 codes
+    per byte) with x_sf (A4).  quantize_x with bfloat16 x asks the library to
+    quantise x first: True or "fp8" -> the A8 format (act_fmt
+    BF16_QUANT_FP8_K32), "fp4" -> the A4 format (BF16_QUANT_FP4_K32).
     Weights uint8 as in include/moefp4.h.  Returns out [T, H] bfloat16
     (default) or float32 (out_dtype=torch.float32)."""
     import torch
     u8 = (torch.uint8,)
     fp8 = (torch.uint8, torch.float8_e4m3fn)
+    quant = {False: None, None: None, True: "fp8", "fp8": "fp8", "fp4": "fp4"}.get(quantize_x, "?")
+    if quant == "?":
+        raise ValueError(f"quantize_x must be False, True, 'fp8' or 'fp4', got {quantize_x!r}")
     a8 = x_sf is not None
     _dev(x, "x", fp8 if a8 else (torch.bfloat16, torch.int16, torch.uint16))
     _dev(x_sf, "x_sf", u8)
@@ -161,16 +170,21 @@ def forward(x, topk_ids, topk_w, w13, w13_sf, w13_gs, w2, w2_sf, w2_gs, gran_k, 
         _dev(t, n, u8)
     _dev(w13_gs, "w13_gs", (torch.float32,))
     _dev(w2_gs, "w2_gs", (torch.float32,))
-    T, H = x.shape
     E, two_i, _ = w13.shape
+    H = w2.shape[1]
+    T, xcols = x.shape
+    a4 = a8 and xcols * 2 == H
+    if xcols != H and not a4:
+        raise ValueError(f"x has {xcols} columns; expected H={H} (or H/2 packed FP4 codes with x_sf)")
     k = topk_ids.shape[1]
     if out_dtype is None:
         out_dtype = torch.bfloat16 if out is None else out.dtype
     if out_dtype not in (torch.bfloat16, torch.float32):
         raise TypeError("out_dtype must be torch.bfloat16 or torch.float32")
-    if quantize_x and a8:
+    if quant and a8:
         raise ValueError("quantize_x takes bfloat16 x without x_sf")
-    act = ACT_FP8_UE8M0_K32 if a8 else (ACT_BF16_QUANT_FP8_K32 if quantize_x else ACT_BF16)
+    act = (ACT_FP4_UE8M0_K32 if a4 else ACT_FP8_UE8M0_K32 if a8 else
+           ACT_BF16_QUANT_FP8_K32 if quant == "fp8" else ACT_BF16_QUANT_FP4_K32 if quant == "fp4" else ACT_BF16)
     p = make_problem(T, E, k, H, two_i // 2, gran_k, act, w13_order,
                      OUT_F32 if out_dtype == torch.float32 else OUT_BF16)
     if out is None:
@@ -183,26 +197,20 @@ def forward(x, topk_ids, topk_w, w13, w13_sf, w13_gs, w2, w2_sf, w2_gs, gran_k, 
     return out
 
 
-def requant_gran_k(src, src_sf, src_gs=None, src_gran=16, dst_gran=32, dst=None, dst_sf=None,
-                   stream=None):
-    """Group16 -> group32 requantisation.  src [E, N, K/2] uint8, src_sf
-    [E, N, K/16] uint8 (E4M3), src_gs [E] float32 or None.  Returns
-    (dst [E, N, K/2], dst_sf [E, N, K/32]); dst may be src (in place)."""
+def quantize_act_fp4(x, x_fp4=None, x_sf=None, stream=None):
+    """bfloat16 [T, H] -> (E2M1 codes [T, H/2] uint8, two per byte, UE8M0
+    scales [T, H/32] uint8), per 32 elements (moe_fp4_quantize_act_fp4)."""
     import torch
-    _dev(src, "src", (torch.uint8,))
-    _dev(src_sf, "src_sf", (torch.uint8,))
-    _dev(src_gs, "src_gs", (torch.float32,))
-    E, N, kh = src.shape
-    K = 2 * kh
-    if dst is None:
-        dst = torch.empty_like(src)
-    if dst_sf is None:
-        dst_sf = torch.empty((E, N, K // dst_gran), dtype=torch.uint8, device=src.device)
-    _dev(dst, "dst", (torch.uint8,))
-    _dev(dst_sf, "dst_sf", (torch.uint8,))
-    _check(lib().fp4_requant_gran_k(E, N, K, _ptr(src), _ptr(src_sf), src_gran, _ptr(src_gs),
-                                    _ptr(dst), _ptr(dst_sf), dst_gran, _stream(stream)))
-    return dst, dst_sf
+    _dev(x, "x", (torch.bfloat16, torch.int16, torch.uint16))
+    T, H = x.shape
+    if x_fp4 is None:
+        x_fp4 = torch.empty((T, H // 2), dtype=torch.uint8, device=x.device)
+    if x_sf is None:
+        x_sf = torch.empty((T, H // 32), dtype=torch.uint8, device=x.device)
+    _dev(x_fp4, "x_fp4", (torch.uint8,))
+    _dev(x_sf, "x_sf", (torch.uint8,))
+    _check(lib().moe_fp4_quantize_act_fp4(T, H, _ptr(x), _ptr(x_fp4), _ptr(x_sf), _stream(stream)))
+    return x_fp4, x_sf
 
 
 def quantize_act(x, x_fp8=None, x_sf=None, stream=None):

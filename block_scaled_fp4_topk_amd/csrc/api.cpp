@@ -44,7 +44,7 @@ struct Layout {
   size_t act_scale, x16, x8, x8_sf, hmax, h, h_sf, y, route_hist, total;
   int route_chunks, route_chunk;
   int tile_m, nt, max_tiles;
-  bool a8, quant_x, g16_a16;
+  bool a8, a4, quant_x, g16_a16;
 };
 
 moefp4_status check_problem(const moefp4_problem* p) {
@@ -58,8 +58,7 @@ moefp4_status check_problem(const moefp4_problem* p) {
   if (p->H <= 0 || p->I <= 0) return fail(MOEFP4_EINVAL, "H and I must be positive");
   if (p->gran_k != 16 && p->gran_k != 32)
     return fail(MOEFP4_EINVAL, "gran_k must be 16 or 32, got %d", p->gran_k);
-  if (p->act_fmt != MOEFP4_ACT_BF16 && p->act_fmt != MOEFP4_ACT_FP8_UE8M0_K32 &&
-      p->act_fmt != MOEFP4_ACT_BF16_QUANT_FP8_K32)
+  if (p->act_fmt < MOEFP4_ACT_BF16 || p->act_fmt > MOEFP4_ACT_BF16_QUANT_FP4_K32)
     return fail(MOEFP4_EINVAL, "unknown act_fmt %d", p->act_fmt);
   if (p->w13_order != MOEFP4_GATE_UP && p->w13_order != MOEFP4_UP_GATE)
     return fail(MOEFP4_EINVAL, "unknown w13_order %d", p->w13_order);
@@ -70,13 +69,22 @@ moefp4_status check_problem(const moefp4_problem* p) {
                 p->H, p->I);
   if (p->act_fmt != MOEFP4_ACT_BF16 && p->gran_k == 16)
     return fail(MOEFP4_EUNSUPPORTED,
-                "FP8 activations with group16 weights (recipe (1,1,16)) are not computed: requantise the "
-                "weights to group32 with fp4_requant_gran_k");
+                "FP8 / FP4 activations with group16 weights (recipe (1,1,16)) are not computed: requantise "
+                "the weights to group32 with fp4_requant_gran_k");
   if (p->H % 256 || p->I % 256)
     return fail(MOEFP4_EUNSUPPORTED, "this build tiles K in chunks of 256: H and I must be multiples of 256, got H=%d I=%d",
                 p->H, p->I);
   const long long A = (long long)p->T * p->top_k;
   if (A > (1LL << 26)) return fail(MOEFP4_EUNSUPPORTED, "T*top_k = %lld exceeds 2^26", A);
+  if (p->act_fmt == MOEFP4_ACT_FP4_UE8M0_K32 || p->act_fmt == MOEFP4_ACT_BF16_QUANT_FP4_K32) {
+    // FP4 activations run on the 128-row GEMM tiles only
+    if (p->H % 512 || p->I % 512)
+      return fail(MOEFP4_EUNSUPPORTED, "FP4 activations need H and I multiples of 512, got H=%d I=%d", p->H,
+                  p->I);
+    if ((long long)p->T * p->H >= (1LL << 31) || A * p->I >= (1LL << 31) ||
+        (long long)p->I * p->H >= (1LL << 31))
+      return fail(MOEFP4_EUNSUPPORTED, "FP4 activations need T*H, T*top_k*I and I*H below 2^31");
+  }
   return MOEFP4_OK;
 }
 
@@ -84,8 +92,10 @@ moefp4_status plan(const moefp4_problem* p, Layout* L) {
   moefp4_status st = check_problem(p);
   if (st != MOEFP4_OK) return st;
   const size_t A = (size_t)p->T * p->top_k, E = p->E, T = p->T, H = p->H, I = p->I;
-  L->quant_x = p->act_fmt == MOEFP4_ACT_BF16_QUANT_FP8_K32;
-  L->a8 = p->act_fmt == MOEFP4_ACT_FP8_UE8M0_K32 || L->quant_x;
+  L->a4 = p->act_fmt == MOEFP4_ACT_FP4_UE8M0_K32 || p->act_fmt == MOEFP4_ACT_BF16_QUANT_FP4_K32;
+  L->quant_x = p->act_fmt == MOEFP4_ACT_BF16_QUANT_FP8_K32 || p->act_fmt == MOEFP4_ACT_BF16_QUANT_FP4_K32;
+  // a8: block-scaled activations (FP8 or FP4) with h quantised the same way
+  L->a8 = p->act_fmt != MOEFP4_ACT_BF16;
   L->g16_a16 = !L->a8 && p->gran_k == 16;
   const size_t active = A < E ? A : E;
   const double avg = active ? (double)A / (double)active : 0.0;
@@ -95,7 +105,7 @@ moefp4_status plan(const moefp4_problem* p, Layout* L) {
   const bool gemm_ok = L->a8 && I % 512 == 0 && H % 512 == 0 &&
                        T * H < (1ull << 31) &&
                        A * I < (1ull << 31) && I * H < (1ull << 31);
-  L->nt = avg > 16.0 ? (gemm_ok ? 8 : 4) : 1;
+  L->nt = L->a4 ? 8 : avg > 16.0 ? (gemm_ok ? 8 : 4) : 1;
   L->tile_m = 16 * L->nt;
   L->max_tiles = (int)(A / L->tile_m + active);
   size_t o = 0;
@@ -109,10 +119,10 @@ moefp4_status plan(const moefp4_problem* p, Layout* L) {
   L->ntiles = take(4);
   L->act_scale = take(L->g16_a16 ? T * 4 : 0);
   L->x16 = take(L->g16_a16 && L->nt != 1 ? T * H * 2 : 0);
-  L->x8 = take(L->quant_x ? T * H : 0);
+  L->x8 = take(L->quant_x ? (L->a4 ? T * H / 2 : T * H) : 0);
   L->x8_sf = take(L->quant_x ? T * (H / 32) : 0);
   L->hmax = take(L->g16_a16 ? A * 4 : 0);
-  L->h = take(L->a8 ? A * I : A * I * 2);
+  L->h = take(L->a4 ? A * I / 2 : L->a8 ? A * I : A * I * 2);
   L->h_sf = take(L->a8 ? A * (I / 32) : 0);
   L->y = take(A * H * 4);
   L->route_chunks = 0;
@@ -158,6 +168,7 @@ moefp4_status route_into(const moefp4_problem* p, const Layout& L, const int32_t
   o.row_scale = row_scale;
   o.x8 = x8;
   o.xsf = x8_sf;
+  o.x_fp4 = L.a4;
   o.nchunks = L.route_chunks;
   o.chunk = L.route_chunk;
   o.hist = L.route_chunks ? at<int32_t>(ws, L.route_hist) : nullptr;
@@ -205,7 +216,7 @@ moefp4_status moe_fp4_forward(const moefp4_problem* p, const void* x, const uint
   if (p->T == 0) return ok();
   if (!x || !topk_ids || !topk_w || !w13 || !w13_sf || !w2 || !w2_sf || !out)
     return fail(MOEFP4_EINVAL, "x, topk_ids, topk_w, w13, w13_sf, w2, w2_sf and out must be non-NULL");
-  if (L.a8 && !L.quant_x && !x_sf) return fail(MOEFP4_EINVAL, "FP8 activations need x_sf");
+  if (L.a8 && !L.quant_x && !x_sf) return fail(MOEFP4_EINVAL, "FP8 / FP4 activations need x_sf");
   if ((!L.a8 || L.quant_x) && x_sf)
     return fail(MOEFP4_EINVAL, "x_sf must be NULL for bfloat16 activations");
   if (misaligned(x, 16) || misaligned(w13, 16) || misaligned(w2, 16) || misaligned(out, 16) ||
@@ -227,8 +238,8 @@ moefp4_status moe_fp4_forward(const moefp4_problem* p, const void* x, const uint
   // computes the per-token fp16 staging scales, and FC1 converts while staging
   const bool stage_f16 = L.g16_a16 && L.nt == 1;
   float* xs = L.g16_a16 ? at<float>(workspace, L.act_scale) : nullptr;
-  // bf16 x to be quantised to FP8 + UE8M0 per 32: also done by the route
-  // launch, into the workspace
+  // bf16 x to be quantised to FP8 or MXFP4 (+ UE8M0 per 32): also done by
+  // the route launch, into the workspace
   uint8_t* x8 = L.quant_x ? at<uint8_t>(workspace, L.x8) : nullptr;
   uint8_t* x8_sf = L.quant_x ? at<uint8_t>(workspace, L.x8_sf) : nullptr;
   st = route_into(p, L, topk_ids, counts, offsets, sorted, slot_of, workspace, hmax,
@@ -262,7 +273,7 @@ moefp4_status moe_fp4_forward(const moefp4_problem* p, const void* x, const uint
     a.h_sf_out = at<uint8_t>(workspace, L.h_sf);
     stage_mark(2, stream);
     st = hip_status(L.nt == 1   ? moefp4::launch_fc_decode(a, 2, true, L.max_tiles, stream)
-                    : L.nt == 8 ? moefp4::launch_fc_gemm_a8(a, true, L.max_tiles, stream)
+                    : L.nt == 8 ? moefp4::launch_fc_gemm_a8(a, true, L.a4, L.max_tiles, stream)
                         : moefp4::launch_fc1_a8(a, L.nt, L.max_tiles, stream),
                     "fc1");
   } else {
@@ -307,7 +318,7 @@ moefp4_status moe_fp4_forward(const moefp4_problem* p, const void* x, const uint
   a.y_out = at<float>(workspace, L.y);
   const int mode = L.a8 ? 2 : (p->gran_k == 16 ? 0 : 1);
   st = hip_status(L.nt == 1   ? moefp4::launch_fc_decode(a, mode, false, L.max_tiles, stream)
-                  : L.nt == 8 ? moefp4::launch_fc_gemm_a8(a, false, L.max_tiles, stream)
+                  : L.nt == 8 ? moefp4::launch_fc_gemm_a8(a, false, L.a4, L.max_tiles, stream)
                   : L.a8 ? moefp4::launch_fc2_a8(a, L.nt, L.max_tiles, stream)
                              : moefp4::launch_fc2_a16(a, p->gran_k, L.nt, L.max_tiles, stream),
                   "fc2");
@@ -367,8 +378,22 @@ moefp4_status moe_fp4_quantize_act(int64_t T, int64_t H, const void* x, uint8_t*
   if (misaligned(x, 16) || misaligned(x_fp8, 16))
     return fail(MOEFP4_EINVAL, "x and x_fp8 must be 16-byte aligned");
   moefp4_status st = hip_status(moefp4::launch_quantize_act(static_cast<const uint16_t*>(x), T, (int)H,
-                                                            x_fp8, x_sf, stream),
+                                                            x_fp8, x_sf, false, stream),
                                 "quantize_act");
+  return st == MOEFP4_OK ? ok() : st;
+}
+
+moefp4_status moe_fp4_quantize_act_fp4(int64_t T, int64_t H, const void* x, uint8_t* x_fp4,
+                                       uint8_t* x_sf, hipStream_t stream) {
+  if (T < 0 || H <= 0 || H % 32) return fail(MOEFP4_EINVAL, "need T >= 0 and H a positive multiple of 32, got T=%lld H=%lld", (long long)T, (long long)H);
+  if (H > (1 << 30) || T > (1ll << 40) / H) return fail(MOEFP4_EUNSUPPORTED, "T*H too large");
+  if (T == 0) return ok();
+  if (!x || !x_fp4 || !x_sf) return fail(MOEFP4_EINVAL, "x, x_fp4 and x_sf must be non-NULL");
+  if (misaligned(x, 16) || misaligned(x_fp4, 16))
+    return fail(MOEFP4_EINVAL, "x and x_fp4 must be 16-byte aligned");
+  moefp4_status st = hip_status(moefp4::launch_quantize_act(static_cast<const uint16_t*>(x), T, (int)H,
+                                                            x_fp4, x_sf, true, stream),
+                                "quantize_act_fp4");
   return st == MOEFP4_OK ? ok() : st;
 }
 

@@ -106,6 +106,15 @@ __device__ __forceinline__ int ceil_log2_over_448(float a) {
   return E - 8 + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0);
 }
 
+// Smallest e with 6 * 2**e >= a (a > 0): a = M * 2**E, M in [1, 2): 6 =
+// 1.5 * 2**2, so e = E - 2 + (M > 1.5).  FP32 subnormal a gives e <= -128
+// (callers clamp to -127).
+__device__ __forceinline__ int ceil_log2_over_6(float a) {
+  uint32_t b = f2u(a);
+  int E = (int)(b >> 23) - 127;
+  return E - 2 + ((b & 0x7FFFFFu) > 0x400000u ? 1 : 0);
+}
+
 // E4M3 (fn) round-to-nearest-even encode of |y| <= 448, sign kept: normals
 // (|y| >= 2**-6) round the 23-bit mantissa to 3 bits, subnormals round to a
 // multiple of 2**-9.

@@ -28,9 +28,11 @@ struct RouteOut {
   int T, H;
   float* row_scale;
   // optional: FP8 + UE8M0 per 32 quantisation of bf16 rows x [T, H] into
-  // x8 [T, H] and xsf [T, H/32] (x8 null: not computed)
+  // x8 [T, H] and xsf [T, H/32] (x8 null: not computed); x_fp4: MXFP4
+  // (E2M1 + UE8M0 per 32) instead, x8 [T, H/2]
   uint8_t* x8;
   uint8_t* xsf;
+  bool x_fp4;
   // multi-workgroup form (nchunks > 0): chunks of `chunk` assignments and a
   // [nchunks][E + 1] int32 scratch for their histograms / starts
   int nchunks, chunk;
@@ -51,9 +53,10 @@ hipError_t launch_route(const int32_t* topk_ids, int A, int E, int tile_m, const
 
 // bf16 [T, H] -> E4M3 [T, H] + UE8M0 [T, H/32]: per 32 elements e =
 // ceil(log2(amax / 448)) (amax == 0: e = -127), clamped to [-127, 127],
-// codes RNE(x / 2**e), sign kept.  H % 32 == 0.
-hipError_t launch_quantize_act(const uint16_t* x, long long T, int H, uint8_t* x8, uint8_t* xsf,
-                               hipStream_t s);
+// codes RNE(x / 2**e), sign kept.  fp4: MXFP4 instead, E2M1 [T, H/2] (two
+// per byte, even element low) with e = ceil(log2(amax / 6)).  H % 32 == 0.
+hipError_t launch_quantize_act(const uint16_t* x, long long T, int H, uint8_t* xq, uint8_t* xsf,
+                               bool fp4, hipStream_t s);
 
 // bf16 [T, H] -> fp16 [T, H] * 2**-p_t with p_t chosen per row so the row
 // maximum lands in [2**14, 2**15); scale[t] = 2**p_t.
@@ -91,9 +94,10 @@ hipError_t launch_fc2_a8(const FcArgs& a, int nt, int max_tiles, hipStream_t s);
 hipError_t launch_fc_decode(const FcArgs& a, int mode, bool fc1, int max_tiles, hipStream_t s);
 
 // Prefill-shaped FP8 x FP4 grouped GEMMs on 128-row expert tiles (direct-
-// to-LDS pipelined, 256 weight rows per workgroup).  Needs H % 512 == 0,
-// I % 512 == 0 and 32-bit row offsets.
-hipError_t launch_fc_gemm_a8(const FcArgs& a, bool fc1, int max_tiles, hipStream_t s);
+// to-LDS pipelined, 256 weight rows per workgroup); a4: MXFP4 activations
+// (act [rows, K/2], h written as MXFP4).  Needs H % 512 == 0, I % 512 == 0
+// and 32-bit row offsets.
+hipError_t launch_fc_gemm_a8(const FcArgs& a, bool fc1, bool a4, int max_tiles, hipStream_t s);
 
 // out[t, :] = sum_j w[t, j] * y[slot_of[t*k + j], :]  (f32, or rounded to bf16)
 hipError_t launch_combine(const float* y, const int32_t* slot_of, const float* topk_w, int T,

@@ -50,11 +50,16 @@ struct alignas(16) Stage {
 };
 // s_waitcnt with vmcnt(n), expcnt and lgkmcnt at their maxima (gfx9 encoding)
 #define WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x0F70)
-constexpr int kOps = 8;       // operand load instructions per wave per stage
+// operand load instructions per wave per stage: 4 weight + 4 activation
+// (FP8: 128 tokens x 128 bytes), or + 2 (A4: 128 tokens x 64 bytes)
+template <bool A4> constexpr int kOpsOf = A4 ? 6 : 8;
 constexpr int kScaleOps = 12;  // scale load instructions per wave per group (8 weight, 4 activation)
 
-template <bool FC1>
+// A4: MXFP4 activations (E2M1 + UE8M0 per 32, K/2 bytes per row) and h
+// quantised to MXFP4 by FC1; both MFMA operands FP4.
+template <bool FC1, bool A4>
 __global__ __launch_bounds__(256, 1) void fc_gemm_a8_kernel(FcArgs a, int nblk) {
+  constexpr int kOps = kOpsOf<A4>;
   __shared__ Stage st0, st1, st2, st3;
   __shared__ int s_src[GM];
 
@@ -101,8 +106,16 @@ __global__ __launch_bounds__(256, 1) void fc_gemm_a8_kernel(FcArgs a, int nblk) 
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int S = 256 * wave + 64 * i + lane;
-    const int t = S >> 3, p = (S & 7) ^ ((t >> 1) & 7);
-    aoff[i] = s_src[t] * K + 16 * p;
+    if (!A4) {
+      const int t = S >> 3, p = (S & 7) ^ ((t >> 1) & 7);
+      aoff[i] = s_src[t] * K + 16 * p;
+    } else {
+      // A4 activations: token t, piece p (K 32p..32p+31) at slot 4 t + (p ^
+      // ((t >> 2) & 3)), the weights' layout; 2 instructions per wave
+      const int S4 = 128 * wave + 64 * (i & 1) + lane;
+      const int t = S4 >> 2, p = (S4 & 3) ^ ((t >> 2) & 3);
+      aoff[i] = s_src[t] * (K >> 1) + 16 * p;
+    }
     const int r = S >> 2, pw = (S & 3) ^ ((r >> 2) & 3);
     woff[i] = wrow(r) * (K >> 1) + 16 * pw;
   }
@@ -111,7 +124,11 @@ __global__ __launch_bounds__(256, 1) void fc_gemm_a8_kernel(FcArgs a, int nblk) 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int S0 = 256 * wave + 64 * i;  // wave-uniform first slot
-      __builtin_amdgcn_global_load_lds(act + (aoff[i] + k0), &b.act[S0 * 16], 16, 0, 0);
+      if (!A4)
+        __builtin_amdgcn_global_load_lds(act + (aoff[i] + k0), &b.act[S0 * 16], 16, 0, 0);
+      else if (i < 2)
+        __builtin_amdgcn_global_load_lds(act + (aoff[i] + (k0 >> 1)), &b.act[(128 * wave + 64 * i) * 16], 16,
+                                         0, 0);
       __builtin_amdgcn_global_load_lds(wbase + (woff[i] + (k0 >> 1)), &b.w[S0 * 16], 16, 0, 0);
     }
   };
@@ -171,14 +188,19 @@ __global__ __launch_bounds__(256, 1) void fc_gemm_a8_kernel(FcArgs a, int nblk) 
 #pragma unroll
     for (int tg = 0; tg < 4; ++tg) {
       const int tb = 64 * wm + 16 * tg;
-      const uint4 b0 = *reinterpret_cast<const uint4*>(&b.act[128 * tb + la0]);
-      const uint4 b1 = *reinterpret_cast<const uint4*>(&b.act[128 * tb + la1]);
-      const v8i B = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w,
-                     (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+      v8i B;
+      if (A4) {
+        const uint4 b0 = *reinterpret_cast<const uint4*>(&b.act[64 * tb + lw]);
+        B = v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, 0, 0, 0, 0};
+      } else {
+        const uint4 b0 = *reinterpret_cast<const uint4*>(&b.act[128 * tb + la0]);
+        const uint4 b1 = *reinterpret_cast<const uint4*>(&b.act[128 * tb + la1]);
+        B = v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+      }
       const int sb = sbyte(g.a[tg], gs);
 #pragma unroll
       for (int rg = 0; rg < 8; ++rg)
-        acc[rg][tg] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[rg], B, acc[rg][tg], 4, 0, 0,
+        acc[rg][tg] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[rg], B, acc[rg][tg], 4, A4 ? 4 : 0, 0,
                                                                       sbyte(g.w[rg], gs), 0, sb);
     }
   };
@@ -286,18 +308,29 @@ __global__ __launch_bounds__(256, 1) void fc_gemm_a8_kernel(FcArgs a, int nblk) 
           }
         amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
         amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
-        int ex = amax > 0.0f ? ceil_log2_over_448(amax) : -127;
+        int ex = amax > 0.0f ? (A4 ? ceil_log2_over_6(amax) : ceil_log2_over_448(amax)) : -127;
         ex = ex < -127 ? -127 : (ex > 127 ? 127 : ex);
         const float inv = __builtin_ldexpf(1.0f, -ex);
         if (valid) {
           const int ob = nb * 128 + 64 * wn + 32 * j;
-          uint8_t* hrow = static_cast<uint8_t*>(a.h_out) + (size_t)slot * a.I;
+          if (A4) {
+            // E2M1 RNE (hardware conversion, unit scale), two per byte
+            uint8_t* hrow = static_cast<uint8_t*>(a.h_out) + (size_t)slot * (a.I >> 1);
 #pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            uint32_t wv = 0;
+            for (int u = 0; u < 2; ++u) {
+              uint32_t d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, h[u][0] * inv, h[u][1] * inv, 1.0f, 0);
+              d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, h[u][2] * inv, h[u][3] * inv, 1.0f, 1);
+              *reinterpret_cast<uint16_t*>(hrow + ((ob + 16 * u + 4 * q) >> 1)) = (uint16_t)d;
+            }
+          } else {
+            uint8_t* hrow = static_cast<uint8_t*>(a.h_out) + (size_t)slot * a.I;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) wv |= f32_to_e4m3_rne(h[u][i] * inv) << (8 * i);
-            *reinterpret_cast<uint32_t*>(hrow + ob + 16 * u + 4 * q) = wv;
+            for (int u = 0; u < 2; ++u) {
+              uint32_t wv = 0;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) wv |= f32_to_e4m3_rne(h[u][i] * inv) << (8 * i);
+              *reinterpret_cast<uint32_t*>(hrow + ob + 16 * u + 4 * q) = wv;
+            }
           }
           if (q == 0) a.h_sf_out[(size_t)slot * (a.I >> 5) + (ob >> 5)] = (uint8_t)(ex + 127);
         }
@@ -313,7 +346,7 @@ __global__ __launch_bounds__(256, 1) void fc_gemm_a8_kernel(FcArgs a, int nblk) 
   }
 }
 
-template <bool FC1>
+template <bool FC1, bool A4>
 hipError_t launch_one(const FcArgs& a, int max_tiles, hipStream_t s) {
   const int nblk = FC1 ? a.I / 128 : a.H / 256;
   if (max_tiles <= 0 || nblk <= 0) return hipSuccess;
@@ -321,14 +354,15 @@ hipError_t launch_one(const FcArgs& a, int max_tiles, hipStream_t s) {
   // (known on the device only) return at once
   const long long items = (long long)max_tiles * nblk;
   const long long grid = (items + 7) / 8 * 8;
-  hipLaunchKernelGGL((fc_gemm_a8_kernel<FC1>), dim3((unsigned)grid), dim3(256), 0, s, a, nblk);
+  hipLaunchKernelGGL((fc_gemm_a8_kernel<FC1, A4>), dim3((unsigned)grid), dim3(256), 0, s, a, nblk);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_fc_gemm_a8(const FcArgs& a, bool fc1, int max_tiles, hipStream_t s) {
-  return fc1 ? launch_one<true>(a, max_tiles, s) : launch_one<false>(a, max_tiles, s);
+hipError_t launch_fc_gemm_a8(const FcArgs& a, bool fc1, bool a4, int max_tiles, hipStream_t s) {
+  if (a4) return fc1 ? launch_one<true, true>(a, max_tiles, s) : launch_one<false, true>(a, max_tiles, s);
+  return fc1 ? launch_one<true, false>(a, max_tiles, s) : launch_one<false, false>(a, max_tiles, s);
 }
 
 }  // namespace moefp4

@@ -194,28 +194,88 @@ __device__ __forceinline__ void quantize_block32(const uint16_t* __restrict__ sr
   *sf = (uint8_t)(ex + 127);
 }
 
+// MXFP4 quantisation of one 32-element block of a bf16 row (the A4 form,
+// the block rule of the group32 requantisation applied to activations):
+// UE8M0 e = smallest with 6 * 2**e >= amax, clamped to [-127, 127] (amax
+// == 0: -127), E2M1 RNE of x / 2**e with the sign kept.  x / 2**e is exact
+// in FP32 (8 significant bits; a bf16 amax below 2**-126 clamps e to -127,
+// which keeps every x / 2**e a finite FP32 value <= 6).  The RNE encode is
+// the hardware conversion with a unit scale; codes are packed two per byte,
+// element 2j in the low nibble.
+__device__ __forceinline__ void quantize_block32_fp4(const uint16_t* __restrict__ src, uint8_t* dst,
+                                                     uint8_t* sf) {
+  uint4 v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = reinterpret_cast<const uint4*>(src)[i];
+  uint32_t m = 0;  // largest magnitude, as bf16 bits (monotone in the value)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t lo = w[j] & 0x7FFFu, hi = (w[j] >> 16) & 0x7FFFu;
+      m = lo > m ? lo : m;
+      m = hi > m ? hi : m;
+    }
+  }
+  // amax = M * 2**E, M in [1, 2): 6 = 1.5 * 2**2, so e = E - 2 + (M > 1.5);
+  // subnormal (and zero) maxima clamp to -127
+  int ex = -127;
+  if (m >= 0x0080u) {
+    const int E = (int)(m >> 7) - 127;
+    ex = E - 2 + ((m & 0x7Fu) > 0x40u ? 1 : 0);
+    ex = ex < -127 ? -127 : (ex > 127 ? 127 : ex);
+  }
+  const float inv = __builtin_ldexpf(1.0f, -ex);
+  uint32_t q[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+    float f[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f[2 * j] = bf16_to_f32(w[j] & 0xFFFFu) * inv;
+      f[2 * j + 1] = bf16_to_f32(w[j] >> 16) * inv;
+    }
+    uint32_t d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, f[0], f[1], 1.0f, 0);
+    d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, f[2], f[3], 1.0f, 1);
+    d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, f[4], f[5], 1.0f, 2);
+    d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, f[6], f[7], 1.0f, 3);
+    q[i] = d;
+  }
+  *reinterpret_cast<uint4*>(dst) = uint4{q[0], q[1], q[2], q[3]};
+  *sf = (uint8_t)(ex + 127);
+}
+
 // Workgroup b of nb quantises 32-element blocks b * 1024 + tid, then every
-// nb * 1024 further.
+// nb * 1024 further; FP4: MXFP4 (16 code bytes per block), else E4M3 (32).
+template <bool FP4>
 __device__ void quantize_rows_from(const uint16_t* __restrict__ x, long long T, int H,
-                                   uint8_t* __restrict__ x8, uint8_t* __restrict__ xsf, int b,
+                                   uint8_t* __restrict__ xq, uint8_t* __restrict__ xsf, int b,
                                    int nb) {
   const long long nblk = T * (H / 32);
   for (long long i = (long long)b * kRouteThreads + threadIdx.x; i < nblk;
-       i += (long long)nb * kRouteThreads)
-    quantize_block32(x + i * 32, x8 + i * 32, xsf + i);
+       i += (long long)nb * kRouteThreads) {
+    if (FP4) quantize_block32_fp4(x + i * 32, xq + i * 16, xsf + i);
+    else quantize_block32(x + i * 32, xq + i * 32, xsf + i);
+  }
 }
 
+template <bool FP4>
 __global__ __launch_bounds__(kRouteThreads) void quantize_act_kernel(const uint16_t* __restrict__ x,
                                                                      long long T, int H,
-                                                                     uint8_t* __restrict__ x8,
+                                                                     uint8_t* __restrict__ xq,
                                                                      uint8_t* __restrict__ xsf) {
-  quantize_rows_from(x, T, H, x8, xsf, blockIdx.x, gridDim.x);
+  quantize_rows_from<FP4>(x, T, H, xq, xsf, blockIdx.x, gridDim.x);
 }
 
 // Activation preparation done by the extra workgroups of a route launch.
 __device__ void row_prep(const RouteOut& o, int b, int nb) {
   if (o.row_scale) row_scales_from(o, b, nb);
-  if (o.x8) quantize_rows_from(o.x, o.T, o.H, o.x8, o.xsf, b, nb);
+  if (o.x8) {
+    if (o.x_fp4) quantize_rows_from<true>(o.x, o.T, o.H, o.x8, o.xsf, b, nb);
+    else quantize_rows_from<false>(o.x, o.T, o.H, o.x8, o.xsf, b, nb);
+  }
 }
 
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t* __restrict__ ids,
@@ -227,7 +287,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t* __r
   __shared__ int s_cnt[kMaxExperts];
   __shared__ int s_tmp[128];
   __shared__ int s_drop;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x;
   // workgroups past the first compute the per-row staging scales instead
   if (blockIdx.x > 0) {
     row_prep(o, blockIdx.x - 1, gridDim.x - 1);
@@ -386,13 +446,17 @@ hipError_t launch_route(const int32_t* topk_ids, int A, int E, int tile_m, const
   return hipGetLastError();
 }
 
-hipError_t launch_quantize_act(const uint16_t* x, long long T, int H, uint8_t* x8, uint8_t* xsf,
-                               hipStream_t s) {
+hipError_t launch_quantize_act(const uint16_t* x, long long T, int H, uint8_t* xq, uint8_t* xsf,
+                               bool fp4, hipStream_t s) {
   if (T <= 0 || H <= 0) return hipSuccess;
   long long nb = (T * (H / 32) + kRouteThreads - 1) / kRouteThreads;
   nb = nb > 1024 ? 1024 : nb;
-  hipLaunchKernelGGL(quantize_act_kernel, dim3((unsigned)nb), dim3(kRouteThreads), 0, s, x, T, H, x8,
-                     xsf);
+  if (fp4)
+    hipLaunchKernelGGL(quantize_act_kernel<true>, dim3((unsigned)nb), dim3(kRouteThreads), 0, s, x, T, H,
+                       xq, xsf);
+  else
+    hipLaunchKernelGGL(quantize_act_kernel<false>, dim3((unsigned)nb), dim3(kRouteThreads), 0, s, x, T, H,
+                       xq, xsf);
   return hipGetLastError();
 }
 

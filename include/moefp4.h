@@ -59,11 +59,21 @@ typedef enum moefp4_status {
  *   recipe (1, 1, 32) of [P2] Context.
  * BF16_QUANT_FP8_K32: x [T, H] bfloat16, quantised by the library to the
  *   FP8_UE8M0_K32 format (as moe_fp4_quantize_act) before the FP8xFP4
- *   computation; x_sf must be NULL. */
+ *   computation; x_sf must be NULL.
+ * FP4_UE8M0_K32 ("A4"): x [T, H/2] E2M1 codes, two per byte, element 2j in
+ *   the low nibble of byte j, and x_sf [T, H/32] UE8M0 bytes, value = e2m1 *
+ *   2**(sf - 127): MXFP4 activations for the FP4xFP4 path (the "A4 prefill"
+ *   of [P3] prepare_w4a16_modelopt_native_weights, in the block-scaled form
+ *   the matrix instruction consumes).  h is quantised the same way between
+ *   FC1 and FC2.
+ * BF16_QUANT_FP4_K32: x [T, H] bfloat16, quantised by the library to
+ *   FP4_UE8M0_K32 (as moe_fp4_quantize_act_fp4); x_sf must be NULL. */
 typedef enum moefp4_act_fmt {
   MOEFP4_ACT_BF16 = 0,
   MOEFP4_ACT_FP8_UE8M0_K32 = 1,
-  MOEFP4_ACT_BF16_QUANT_FP8_K32 = 2
+  MOEFP4_ACT_BF16_QUANT_FP8_K32 = 2,
+  MOEFP4_ACT_FP4_UE8M0_K32 = 3,
+  MOEFP4_ACT_BF16_QUANT_FP4_K32 = 4
 } moefp4_act_fmt;
 
 /* Order of the 2I rows of w13.  GATE_UP: rows [0, I) are the gate projection
@@ -112,12 +122,15 @@ moefp4_status moe_fp4_route(const moefp4_problem* p, const int32_t* topk_ids,
  * e = topk_ids[t, j]; FC1 uses w13 [E, 2I, H/2] + w13_sf [E, 2I, H/gran]
  * (+ w13_gs [E]), FC2 uses w2 [E, H, I/2] + w2_sf [E, H, I/gran] (+ w2_gs),
  * SwiGLU h = silu(gate) * up; h is rounded to bfloat16 (BF16 activations) or
- * quantised per 32 elements to E4M3 + UE8M0 (FP8 activations) before FC2;
- * FP32 accumulation; out [T, H] bfloat16 or float32 (p->out_fmt).
- * Supported: (BF16, gran 16), (BF16, gran 32), (FP8_UE8M0_K32, gran 32).
- * FP8 activations with group16 weights return EUNSUPPORTED, like the
- * capability gate on recipe (1, 1, 16) in [P1] / [P2] Current patch scope.
- * x_sf must be NULL for BF16 and non-NULL for FP8.  All pointers device
+ * quantised per 32 elements to E4M3 + UE8M0 (FP8 activations) or to E2M1 +
+ * UE8M0 (FP4 activations) before FC2; FP32 accumulation; out [T, H]
+ * bfloat16 or float32 (p->out_fmt).
+ * Supported: (BF16, gran 16), (BF16, gran 32), (FP8, gran 32), (FP4, gran
+ * 32; H and I multiples of 512: FP4 activations always run on the 128-row
+ * GEMM tiles).  FP8 or FP4 activations with group16 weights return
+ * EUNSUPPORTED, like the capability gate on recipe (1, 1, 16) in [P1] / [P2]
+ * Current patch scope.
+ * x_sf must be NULL for BF16 and non-NULL for FP8 / FP4.  All pointers device
  * memory; topk_ids [T, k] int32, topk_w [T, k] float32; x, x_sf, the weight
  * and scale tensors and out 16-byte aligned, the workspace 256-byte aligned
  * (EINVAL otherwise). */
@@ -160,6 +173,20 @@ moefp4_status fp4_requant_gran_k(int64_t E, int64_t N, int64_t K,
  * infinite inputs are outside the contract. */
 moefp4_status moe_fp4_quantize_act(int64_t T, int64_t H, const void* x, uint8_t* x_fp8,
                                    uint8_t* x_sf, hipStream_t stream);
+
+/* Quantise bfloat16 activation rows to the MXFP4 activation format
+ * (FP4_UE8M0_K32): per row, per 32 consecutive elements, UE8M0 scale byte e
+ * + 127 with e the smallest integer such that 6 * 2**e >= max |x| (a block
+ * of zeros gets byte 0; e clamped to [-127, 127]), and E2M1 codes
+ * round-to-nearest-even of x / 2**e, ties to the even code, the sign kept
+ * (also on zero) -- the block rule of fp4_requant_gran_k ([P2]
+ * Requantization path) applied to activations.  x [T, H] bfloat16, x_fp4
+ * [T, H/2] uint8 (element 2j in the low nibble of byte j), x_sf [T, H/32]
+ * uint8, all device memory owned by the caller, x and x_fp4 16-byte
+ * aligned; H a positive multiple of 32 (EINVAL otherwise).  Enqueued on
+ * `stream`.  NaN and infinite inputs are outside the contract. */
+moefp4_status moe_fp4_quantize_act_fp4(int64_t T, int64_t H, const void* x, uint8_t* x_fp4,
+                                       uint8_t* x_sf, hipStream_t stream);
 
 /* Profiling hook.  With events non-NULL and n >= 6, each later
  * moe_fp4_forward call on this thread records, on its stream, events[0]

@@ -138,12 +138,13 @@ def make_routing(cfg: MoEConfig):
 
 def make_activations(cfg: MoEConfig):
     """A16: x ~ N(0,1) cast to bfloat16 (torch RNE cast) -> (bits, None); the
-         same for "bf16q" (bfloat16 x that the library quantises to FP8).
+         same for "bf16q" / "bf16q4" (bfloat16 x that the library quantises
+         to FP8 / MXFP4).
     A8 : per 32-block UE8M0 byte uniform in {119, 120, 121} and E4M3 payload
          = torch cast of clip(64 * N(0,1), +-448) -> (fp8 bytes, sf bytes)."""
     rng = _rng(cfg.seed, _S_X)
     T, H = cfg.T, cfg.H
-    if cfg.act in ("bf16", "bf16q"):
+    if cfg.act in ("bf16", "bf16q", "bf16q4"):
         xf = rng.standard_normal((T, H), dtype=np.float32)
         bits = torch.from_numpy(xf).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
         return bits.copy(), None

@@ -30,7 +30,8 @@ def L():
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
     assert {"moe_fp4_forward", "moe_fp4_route", "fp4_requant_gran_k", "moe_fp4_workspace_bytes",
-            "moe_fp4_quantize_act", "moefp4_last_error", "moefp4_version"} <= set(names)
+            "moe_fp4_quantize_act", "moe_fp4_quantize_act_fp4", "moefp4_last_error",
+            "moefp4_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
     assert b"gfx950" in L.moefp4_version()
@@ -52,6 +53,9 @@ def test_workspace_sizes(L):
     assert st == 0 and n > 512 * 6144 * 4  # holds the f32 FC2 rows
     st8, n8 = ws_status(P(T=8192, gran_k=32, act_fmt=1))
     assert st8 == 0 and n8 > 65536 * 6144 * 4
+    # A4 with the library quantising x: x codes T*H/2 and h codes A*I/2 fit
+    st4, n4 = ws_status(P(T=8192, gran_k=32, act_fmt=4))
+    assert st4 == 0 and n4 > 65536 * 6144 * 4 + 8192 * 6144 // 2 + 65536 * 2048 // 2
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -65,6 +69,10 @@ def test_workspace_sizes(L):
     (dict(I=2080), m.EUNSUPPORTED),
     (dict(act_fmt=1, gran_k=16), m.EUNSUPPORTED),
     (dict(act_fmt=2, gran_k=16), m.EUNSUPPORTED),
+    (dict(act_fmt=3, gran_k=16), m.EUNSUPPORTED),
+    (dict(act_fmt=4, gran_k=16), m.EUNSUPPORTED),
+    (dict(act_fmt=3, gran_k=32, H=6400), m.EUNSUPPORTED),   # FP4 x: H % 512
+    (dict(act_fmt=4, gran_k=32, I=2304), m.EUNSUPPORTED),   # FP4 x: I % 512
     (dict(act_fmt=7), m.EINVAL),
     (dict(w13_order=3), m.EINVAL),
     (dict(out_fmt=2), m.EINVAL),
@@ -119,6 +127,25 @@ def test_quantize_act_rejects_before_launch(L):
     assert q(4, 64, z, g, f, z) == m.EINVAL                       # NULL x
     assert q(4, 64, ctypes.c_void_p((1 << 20) + 8), g, f, z) == m.EINVAL  # misaligned x
     assert q(0, 64, z, z, z, z) == 0                              # empty
+
+
+def test_quantize_act_fp4_rejects_before_launch(L):
+    z = ctypes.c_void_p(0)
+    f = ctypes.c_void_p(1 << 20)
+    g = ctypes.c_void_p(1 << 30)
+    q = L.moe_fp4_quantize_act_fp4
+    assert q(4, 48, f, g, f, z) == m.EINVAL                       # H % 32
+    assert q(4, 64, f, z, f, z) == m.EINVAL                       # NULL x_fp4
+    assert q(4, 64, f, ctypes.c_void_p((1 << 30) + 4), f, z) == m.EINVAL  # misaligned x_fp4
+    assert q(0, 64, z, z, z, z) == 0                              # empty
+
+
+def test_forward_a4_needs_x_sf(L):
+    p = P(gran_k=32, act_fmt=3)
+    f = ctypes.c_void_p(1 << 20)
+    z = ctypes.c_void_p(0)
+    st = L.moe_fp4_forward(ctypes.byref(p), f, z, f, f, f, f, z, f, f, z, f, f, 1 << 40, z)
+    assert st == m.EINVAL and b"x_sf" in L.moefp4_last_error()
 
 
 def test_forward_quant_x_rejects_x_sf(L):
