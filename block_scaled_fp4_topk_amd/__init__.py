@@ -197,6 +197,30 @@ def forward(x, topk_ids, topk_w, w13, w13_sf, w13_gs, w2, w2_sf, w2_gs, gran_k, 
     return out
 
 
+def requant_gran_k(src, src_sf, src_gs=None, src_gran=16, dst_gran=32, dst=None, dst_sf=None,
+                   stream=None):
+    """Group16 -> group32 requantisation.  src [E, N, K/2] uint8, src_sf
+    [E, N, K/16] uint8 (E4M3), src_gs [E] float32 or None.  Returns
+    (dst [E, N, K/2], dst_sf [E, N, K/32]); dst may be src (in place)."""
+    import torch
+    _dev(src, "src", (torch.uint8,))
+    _dev(src_sf, "src_sf", (torch.uint8,))
+    _dev(src_gs, "src_gs", (torch.float32,))
+    E, N, kh = src.shape
+    K = 2 * kh
+    if dst is None:
+        dst = torch.empty_like(src)
+    if dst_sf is None:
+        dst_sf = torch.empty((E, N, K // dst_gran), dtype=torch.uint8, device=src.device)
+    _dev(dst, "dst", (torch.uint8,))
+    _dev(dst_sf, "dst_sf", (torch.uint8,))
+    _check(lib().fp4_requant_gran_k(E, N, K, _ptr(src), _ptr(src_sf), src_gran, _ptr(src_gs),
+                                    _ptr(dst), _ptr(dst_sf), dst_gran, _stream(stream)))
+    return dst, dst_sf
+
+
+
+
 def quantize_act_fp4(x, x_fp4=None, x_sf=None, stream=None):
     """bfloat16 [T, H] -> (E2M1 codes [T, H/2] uint8, two per byte, UE8M0
     scales [T, H/32] uint8), per 32 elements (moe_fp4_quantize_act_fp4)."""

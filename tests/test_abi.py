@@ -37,6 +37,16 @@ def test_exports_every_declared_symbol(L):
     assert b"gfx950" in L.moefp4_version()
 
 
+def test_binding_exports():
+    """Every name the binding lists exists, and each C entry point for users
+    has its Python wrapper (no GPU needed)."""
+    for n in m.__all__:
+        assert hasattr(m, n), n
+    for n in ("forward", "route", "requant_gran_k", "quantize_act", "quantize_act_fp4",
+              "workspace_bytes", "dropped_assignments"):
+        assert callable(getattr(m, n)), n
+
+
 def P(**kw):
     d = dict(T=64, E=256, top_k=8, H=6144, I=2048, gran_k=16, act_fmt=0, w13_order=0, out_fmt=0)
     d.update(kw)
