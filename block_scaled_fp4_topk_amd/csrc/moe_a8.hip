@@ -218,7 +218,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     const int s = slot_of[t * k + j];
     if (s < 0) continue;
     const float wj = w[t * k + j];
-    const float4 v = *reinterpret_cast<const float4*>(y + (size_t)s * H + n);
+    // Y is read once: non-temporal (whole 4 KB row pieces per workgroup)
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(y + (size_t)s * H + n));
     acc.x += wj * v.x;
     acc.y += wj * v.y;
     acc.z += wj * v.z;
