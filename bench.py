@@ -35,13 +35,15 @@ PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "fp8": 5000.0, "fp4": 10100.0}
 WORKLOAD_TEXT = {
     "decode16": "W4A16 NVFP4 decode: T=64 E=256 top-8 H=6144 I=2048, bf16 x, E2M1 + E4M3 k16 + fp32 global",
     "decode32": "FP8xFP4 decode: T=256 E=256 top-8 H=6144 I=2048, E4M3+UE8M0 k32 x, E2M1 + UE8M0 k32",
+    "decode32_a4": "A4 decode: T=256 E=256 top-8 H=6144 I=2048, bf16 x quantised by the library to MXFP4 "
+                   "(E2M1+UE8M0 k32), h MXFP4, E2M1 + UE8M0 k32 weights",
     "prefill32": "prefill: T=8192 E=256 top-8 Zipf(1.1) H=6144 I=2048, E4M3+UE8M0 k32 x, E2M1 + UE8M0 k32",
     "prefill32_bf16q": "prefill: T=8192 E=256 top-8 Zipf(1.1) H=6144 I=2048, bf16 x quantised by the "
                        "library to E4M3+UE8M0 k32, E2M1 + UE8M0 k32",
     "prefill32_a4": "A4 prefill: T=8192 E=256 top-8 Zipf(1.1) H=6144 I=2048, bf16 x quantised by the "
                     "library to MXFP4 (E2M1+UE8M0 k32), h MXFP4, E2M1 + UE8M0 k32 weights",
 }
-DTYPE = {"decode16": "f16", "decode32": "fp8xfp4", "prefill32": "fp8xfp4", "prefill32_bf16q": "fp8xfp4",
+DTYPE = {"decode16": "f16", "decode32": "fp8xfp4", "decode32_a4": "fp4xfp4", "prefill32": "fp8xfp4", "prefill32_bf16q": "fp8xfp4",
          "prefill32_a4": "fp4xfp4"}
 STAGES = ["route", "act_prep", "fc1_swiglu", "fc2", "combine"]
 
@@ -110,10 +112,10 @@ def stage_kernel(cfg, ids, stage):
     A = ids.size
     active = len(np.unique(ids[ids >= 0]))
     a4 = cfg.act == "bf16q4"
-    mode = 2 if cfg.act in ("fp8", "bf16q", "bf16q4") else (0 if cfg.gran == 16 else 1)
-    gemm_ok = (mode == 2 and cfg.I % 512 == 0 and cfg.H % 512 == 0 and cfg.T * cfg.H < 2**31
+    mode = 3 if a4 else 2 if cfg.act in ("fp8", "bf16q") else (0 if cfg.gran == 16 else 1)
+    gemm_ok = (mode >= 2 and cfg.I % 512 == 0 and cfg.H % 512 == 0 and cfg.T * cfg.H < 2**31
                and A * cfg.I < 2**31 and cfg.I * cfg.H < 2**31)
-    nt = 8 if a4 else (8 if gemm_ok else 4) if active and A / active > 16 else 1
+    nt = (8 if gemm_ok else 4) if active and A / active > 16 else 1
     if nt == 8:
         return (f"fc_gemm_a8_kernel<{'true' if stage == 'fc1_swiglu' else 'false'}, "
                 f"{'true' if a4 else 'false'}>")
@@ -128,8 +130,8 @@ def workload_cfg(synth, name):
     take bfloat16 x that the library quantises)."""
     if name in synth.CONFIGS:
         return synth.CONFIGS[name]
-    return synth.variant(synth.CONFIGS["prefill32"], name=name,
-                         act="bf16q4" if name.endswith("_a4") else "bf16q")
+    base, _, form = name.partition("_")
+    return synth.variant(synth.CONFIGS[base], name=name, act="bf16q4" if form == "a4" else "bf16q")
 
 
 def kernel_file_key(symbol):
@@ -361,7 +363,7 @@ def secondary(moe, torch, synth, args, inp16, d16):
                             "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
     del src13, sf13, gs13, src2, sf2, gs2, d13, s13, d2, s2
     torch.cuda.empty_cache()
-    for name in ("decode32", "prefill32", "prefill32_bf16q", "prefill32_a4"):
+    for name in ("decode32", "decode32_a4", "prefill32", "prefill32_bf16q", "prefill32_a4"):
         cfg = workload_cfg(synth, name)
         print(f"[bench] secondary {name}", file=sys.stderr, flush=True)
         inp = synth.make_moe_inputs(cfg)

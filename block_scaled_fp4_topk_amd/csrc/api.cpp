@@ -77,7 +77,7 @@ moefp4_status check_problem(const moefp4_problem* p) {
   const long long A = (long long)p->T * p->top_k;
   if (A > (1LL << 26)) return fail(MOEFP4_EUNSUPPORTED, "T*top_k = %lld exceeds 2^26", A);
   if (p->act_fmt == MOEFP4_ACT_FP4_UE8M0_K32 || p->act_fmt == MOEFP4_ACT_BF16_QUANT_FP4_K32) {
-    // FP4 activations run on the 128-row GEMM tiles only
+    // FP4 activations beyond decode sizes run on the 128-row GEMM tiles only
     if (p->H % 512 || p->I % 512)
       return fail(MOEFP4_EUNSUPPORTED, "FP4 activations need H and I multiples of 512, got H=%d I=%d", p->H,
                   p->I);
@@ -105,7 +105,7 @@ moefp4_status plan(const moefp4_problem* p, Layout* L) {
   const bool gemm_ok = L->a8 && I % 512 == 0 && H % 512 == 0 &&
                        T * H < (1ull << 31) &&
                        A * I < (1ull << 31) && I * H < (1ull << 31);
-  L->nt = L->a4 ? 8 : avg > 16.0 ? (gemm_ok ? 8 : 4) : 1;
+  L->nt = avg > 16.0 ? (gemm_ok ? 8 : 4) : 1;
   L->tile_m = 16 * L->nt;
   L->max_tiles = (int)(A / L->tile_m + active);
   size_t o = 0;
@@ -272,7 +272,7 @@ moefp4_status moe_fp4_forward(const moefp4_problem* p, const void* x, const uint
     a.act_sf = L.quant_x ? x8_sf : x_sf;
     a.h_sf_out = at<uint8_t>(workspace, L.h_sf);
     stage_mark(2, stream);
-    st = hip_status(L.nt == 1   ? moefp4::launch_fc_decode(a, 2, true, L.max_tiles, stream)
+    st = hip_status(L.nt == 1   ? moefp4::launch_fc_decode(a, L.a4 ? 3 : 2, true, L.max_tiles, stream)
                     : L.nt == 8 ? moefp4::launch_fc_gemm_a8(a, true, L.a4, L.max_tiles, stream)
                         : moefp4::launch_fc1_a8(a, L.nt, L.max_tiles, stream),
                     "fc1");
@@ -316,7 +316,7 @@ moefp4_status moe_fp4_forward(const moefp4_problem* p, const void* x, const uint
   a.h_out = nullptr;
   a.h_sf_out = nullptr;
   a.y_out = at<float>(workspace, L.y);
-  const int mode = L.a8 ? 2 : (p->gran_k == 16 ? 0 : 1);
+  const int mode = L.a4 ? 3 : L.a8 ? 2 : (p->gran_k == 16 ? 0 : 1);
   st = hip_status(L.nt == 1   ? moefp4::launch_fc_decode(a, mode, false, L.max_tiles, stream)
                   : L.nt == 8 ? moefp4::launch_fc_gemm_a8(a, false, L.a4, L.max_tiles, stream)
                   : L.a8 ? moefp4::launch_fc2_a8(a, L.nt, L.max_tiles, stream)

@@ -89,7 +89,8 @@ hipError_t launch_fc1_a8(const FcArgs& a, int nt, int max_tiles, hipStream_t s);
 hipError_t launch_fc2_a8(const FcArgs& a, int nt, int max_tiles, hipStream_t s);
 
 // Decode-shaped FC kernels (expert tiles of <= 16 activation rows); mode 0:
-// bf16 x group16, 1: bf16 x group32, 2: FP8 x group32.  Needs K % 256 == 0,
+// bf16 x group16, 1: bf16 x group32, 2: FP8 x group32, 3: MXFP4 x group32
+// (act [rows, K/2], h written as MXFP4).  Needs K % 256 == 0,
 // I % 64 == 0 (FC1) and H % 128 == 0 (FC2).
 hipError_t launch_fc_decode(const FcArgs& a, int mode, bool fc1, int max_tiles, hipStream_t s);
 

@@ -3,6 +3,8 @@
 //   MODE 0  bf16 activations, group16 E4M3 weights   -> fp16 MFMA
 //   MODE 1  bf16 activations, group32 UE8M0 weights  -> bf16 MFMA
 //   MODE 2  FP8 + UE8M0 activations, group32 weights -> block-scaled MFMA
+//   MODE 3  MXFP4 activations (A4), group32 weights  -> block-scaled MFMA,
+//           both operands FP4
 // (the W4A16 forms of b12x moe/fused/w4a16/prepare.py and the FP8xFP4
 // recipe (1, 1, 32) of the GLM-5.2 NVFP4 group16 MegaMoE notes, Context).
 //
@@ -68,9 +70,10 @@ __device__ __forceinline__ int sc_swz(int lr) { return (lr >> 1) & 7; }
 template <int MODE, bool FC1>
 __global__ __launch_bounds__(256, (MODE == 0 && FC1) ? 2 : 3) void fc_decode_kernel(FcArgs a) {
   constexpr bool RING2 = MODE == 0 && FC1;
-  constexpr int ESZ = MODE == 2 ? 1 : 2;               // activation element bytes
-  constexpr int AROW = KC * ESZ + 16;                  // staged activation row stride
-  constexpr int SEGB = KC * ESZ / 16;                  // activation bytes per thread (32 or 16)
+  constexpr bool SCALED = MODE >= 2;                   // block-scaled activations (FP8 or FP4)
+  constexpr int ACB = MODE == 3 ? KC / 2 : MODE == 2 ? KC : 2 * KC;  // activation bytes per row per chunk
+  constexpr int AROW = ACB + 16;                       // staged activation row stride
+  constexpr int SEGB = ACB / 16;                       // activation bytes per thread (32, 16 or 8)
   constexpr int SCB = MODE == 0 ? KC / 16 : KC / 32;   // weight-scale bytes per row per chunk
   constexpr int SG = 128 / SCB;                        // chunks per scale group
   constexpr int RPC = WR / SG;                         // scale lines staged per chunk (16 or 8)
@@ -185,15 +188,20 @@ __global__ __launch_bounds__(256, (MODE == 0 && FC1) ? 2 : 3) void fc_decode_ker
   const int ssrc = s_src[sr];
   const float sinv = 1.0f / s_rs[sr];
   const uint8_t* act = static_cast<const uint8_t*>(a.act);
-  const uint8_t* arow_p = act + (size_t)(ssrc >= 0 ? ssrc : 0) * ((size_t)K * ESZ) + ss * SEGB;
-  const uint8_t* asf_p = MODE == 2 ? a.act_sf + (size_t)(ssrc >= 0 ? ssrc : 0) * (K >> 5) : nullptr;
+  const uint8_t* arow_p = act + (size_t)(ssrc >= 0 ? ssrc : 0) * ((size_t)(K / KC) * ACB) + ss * SEGB;
+  const uint8_t* asf_p = SCALED ? a.act_sf + (size_t)(ssrc >= 0 ? ssrc : 0) * (K >> 5) : nullptr;
   uint4 av0 = {0u, 0u, 0u, 0u}, av1 = {0u, 0u, 0u, 0u};
   uint2 avs = {0u, 0u};
   auto load_act = [&](int c) __attribute__((always_inline)) {
     if (ssrc >= 0) {
-      av0 = *reinterpret_cast<const uint4*>(arow_p + (size_t)c * (KC * ESZ));
-      if (SEGB == 32) av1 = *reinterpret_cast<const uint4*>(arow_p + (size_t)c * (KC * ESZ) + 16);
-      if (MODE == 2 && ss == 0) avs = *reinterpret_cast<const uint2*>(asf_p + c * (KC / 32));
+      if (SEGB == 8) {
+        const uint2 v = *reinterpret_cast<const uint2*>(arow_p + (size_t)c * ACB);
+        av0 = uint4{v.x, v.y, 0u, 0u};
+      } else {
+        av0 = *reinterpret_cast<const uint4*>(arow_p + (size_t)c * ACB);
+      }
+      if (SEGB == 32) av1 = *reinterpret_cast<const uint4*>(arow_p + (size_t)c * ACB + 16);
+      if (SCALED && ss == 0) avs = *reinterpret_cast<const uint2*>(asf_p + c * (KC / 32));
     }
   };
 
@@ -238,9 +246,10 @@ __global__ __launch_bounds__(256, (MODE == 0 && FC1) ? 2 : 3) void fc_decode_ker
         v1 = uint4{w[4], w[5], w[6], w[7]};
       }
       uint8_t* d = sb + sr * AROW + ss * SEGB;
-      *reinterpret_cast<uint4*>(d) = v0;
+      if (SEGB == 8) *reinterpret_cast<uint2*>(d) = uint2{v0.x, v0.y};
+      else *reinterpret_cast<uint4*>(d) = v0;
       if (SEGB == 32) *reinterpret_cast<uint4*>(d + 16) = v1;
-      if (MODE == 2 && ss == 0) *reinterpret_cast<uint2*>(sbsf + sr * 8) = avs;
+      if (SCALED && ss == 0) *reinterpret_cast<uint2*>(sbsf + sr * 8) = avs;
     }
     // also waits for this chunk's weight and scale loads; every wave is past
     // the previous chunk, so the other buffers and the scale lines read at
@@ -295,12 +304,17 @@ __global__ __launch_bounds__(256, (MODE == 0 && FC1) ? 2 : 3) void fc_decode_ker
     const uint8_t* brow = sb + r16 * AROW;
     uint4 bv[8];
     int sbb0 = 0, sbb1 = 0;
-    if (MODE == 2) {
+    if (SCALED) {
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        const int o = 64 * (q >> 1) + 32 * st + 16 * (q & 1);
-        bv[2 * st] = *reinterpret_cast<const uint4*>(brow + o);
-        bv[2 * st + 1] = *reinterpret_cast<const uint4*>(brow + 128 + o);
+        if (MODE == 3) {
+          // FP4 operand: hardware block q of step st = memory block 2 q + st
+          bv[2 * st] = *reinterpret_cast<const uint4*>(brow + 16 * (2 * q + st));
+        } else {
+          const int o = 64 * (q >> 1) + 32 * st + 16 * (q & 1);
+          bv[2 * st] = *reinterpret_cast<const uint4*>(brow + o);
+          bv[2 * st + 1] = *reinterpret_cast<const uint4*>(brow + 128 + o);
+        }
       }
       const uint32_t sbb = *reinterpret_cast<const uint16_t*>(sbsf + r16 * 8 + 2 * q);
       sbb0 = (int)(sbb & 0xFFu);
@@ -317,21 +331,25 @@ __global__ __launch_bounds__(256, (MODE == 0 && FC1) ? 2 : 3) void fc_decode_ker
       }
       if (c / SG + 1 < ngroups) issue_sc_slice(c / SG + 1, j);
     }
-    if (MODE == 2) {
+    if (SCALED) {
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         const uint4& ca = st ? w0b : w0a;
         const uint4& cb = st ? w1b : w1a;
-        const v8i B = {(int)bv[2 * st].x, (int)bv[2 * st].y, (int)bv[2 * st].z, (int)bv[2 * st].w,
-                       (int)bv[2 * st + 1].x, (int)bv[2 * st + 1].y, (int)bv[2 * st + 1].z,
-                       (int)bv[2 * st + 1].w};
+        const v8i B = MODE == 3 ? v8i{(int)bv[2 * st].x, (int)bv[2 * st].y, (int)bv[2 * st].z,
+                                      (int)bv[2 * st].w, 0, 0, 0, 0}
+                                : v8i{(int)bv[2 * st].x, (int)bv[2 * st].y, (int)bv[2 * st].z,
+                                      (int)bv[2 * st].w, (int)bv[2 * st + 1].x, (int)bv[2 * st + 1].y,
+                                      (int)bv[2 * st + 1].z, (int)bv[2 * st + 1].w};
         const v8i A0 = {(int)ca.x, (int)ca.y, (int)ca.z, (int)ca.w, 0, 0, 0, 0};
         const v8i A1 = {(int)cb.x, (int)cb.y, (int)cb.z, (int)cb.w, 0, 0, 0, 0};
         const int sa0 = (int)((s0 >> (8 * st)) & 0xFFu);
         const int sa1 = (int)((s1 >> (8 * st)) & 0xFFu);
         const int sbv = st ? sbb1 : sbb0;
-        acc0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A0, B, acc0, 4, 0, 0, sa0, 0, sbv);
-        acc1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A1, B, acc1, 4, 0, 0, sa1, 0, sbv);
+        acc0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A0, B, acc0, 4, MODE == 3 ? 4 : 0, 0, sa0, 0,
+                                                                sbv);
+        acc1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A1, B, acc1, 4, MODE == 3 ? 4 : 0, 0, sa1, 0,
+                                                                sbv);
       }
     } else if (MODE == 0) {
       // group16 scale of MFMA j: byte j / 2 of s0 / s1
@@ -385,22 +403,30 @@ __global__ __launch_bounds__(256, (MODE == 0 && FC1) ? 2 : 3) void fc_decode_ker
       h[i] = swiglu(acc0[i] * cs, acc1[i] * cs);
       amax = fmaxf(amax, fabsf(h[i]));
     }
-    if (MODE == 2) {
+    if (SCALED) {
       // the 32-wide quantisation block spans this wave and its partner
       amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
       amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
       if (q == 0) s_amax[wave][r16] = amax;
       __syncthreads();
       amax = fmaxf(s_amax[wave][r16], s_amax[wave ^ 1][r16]);
-      int ex = amax > 0.0f ? ceil_log2_over_448(amax) : -127;
+      int ex = amax > 0.0f ? (MODE == 3 ? ceil_log2_over_6(amax) : ceil_log2_over_448(amax)) : -127;
       ex = ex < -127 ? -127 : (ex > 127 ? 127 : ex);
       const float inv = __builtin_ldexpf(1.0f, -ex);
       if (valid) {
-        uint32_t wv = 0;
+        if (MODE == 3) {
+          // E2M1 RNE (hardware conversion, unit scale), two per byte
+          uint32_t d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, h[0] * inv, h[1] * inv, 1.0f, 0);
+          d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, h[2] * inv, h[3] * inv, 1.0f, 1);
+          uint8_t* hrow = static_cast<uint8_t*>(a.h_out) + (size_t)slot * (a.I >> 1);
+          *reinterpret_cast<uint16_t*>(hrow + ((obase + 4 * q) >> 1)) = (uint16_t)d;
+        } else {
+          uint32_t wv = 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) wv |= f32_to_e4m3_rne(h[i] * inv) << (8 * i);
-        uint8_t* hrow = static_cast<uint8_t*>(a.h_out) + (size_t)slot * a.I;
-        *reinterpret_cast<uint32_t*>(hrow + obase + 4 * q) = wv;
+          for (int i = 0; i < 4; ++i) wv |= f32_to_e4m3_rne(h[i] * inv) << (8 * i);
+          uint8_t* hrow = static_cast<uint8_t*>(a.h_out) + (size_t)slot * a.I;
+          *reinterpret_cast<uint32_t*>(hrow + obase + 4 * q) = wv;
+        }
         if (q == 0 && (wave & 1) == 0)
           a.h_sf_out[(size_t)slot * (a.I >> 5) + (obase >> 5)] = (uint8_t)(ex + 127);
       }
@@ -448,11 +474,13 @@ hipError_t launch_fc_decode(const FcArgs& a, int mode, bool fc1, int max_tiles, 
   if (fc1) {
     if (mode == 0) return launch_one<0, true>(a, max_tiles, s);
     if (mode == 1) return launch_one<1, true>(a, max_tiles, s);
-    return launch_one<2, true>(a, max_tiles, s);
+    if (mode == 2) return launch_one<2, true>(a, max_tiles, s);
+    return launch_one<3, true>(a, max_tiles, s);
   }
   if (mode == 0) return launch_one<0, false>(a, max_tiles, s);
   if (mode == 1) return launch_one<1, false>(a, max_tiles, s);
-  return launch_one<2, false>(a, max_tiles, s);
+  if (mode == 2) return launch_one<2, false>(a, max_tiles, s);
+  return launch_one<3, false>(a, max_tiles, s);
 }
 
 }  // namespace moefp4

@@ -126,8 +126,7 @@ moefp4_status moe_fp4_route(const moefp4_problem* p, const int32_t* topk_ids,
  * UE8M0 (FP4 activations) before FC2; FP32 accumulation; out [T, H]
  * bfloat16 or float32 (p->out_fmt).
  * Supported: (BF16, gran 16), (BF16, gran 32), (FP8, gran 32), (FP4, gran
- * 32; H and I multiples of 512: FP4 activations always run on the 128-row
- * GEMM tiles).  FP8 or FP4 activations with group16 weights return
+ * 32; H and I multiples of 512, the shapes of the FP8 / FP4 GEMM tiles).  FP8 or FP4 activations with group16 weights return
  * EUNSUPPORTED, like the capability gate on recipe (1, 1, 16) in [P1] / [P2]
  * Current patch scope.
  * x_sf must be NULL for BF16 and non-NULL for FP8 / FP4.  All pointers device

@@ -2,8 +2,9 @@
 FP4 x FP4 block-scaled MFMA) against the oracle: the bfloat16 -> MXFP4
 quantiser bit-exact over the whole finite bfloat16 range (zeros, signed
 zeros, subnormals, blocks of zeros, rounding ties), and the forward with
-caller-quantised and library-quantised x at prefill and decode shapes and at
-the full prefill size on sampled tokens, within the stated bound around the
+caller-quantised and library-quantised x at prefill and decode shapes (the
+128-row GEMM tiles and the 16-row decode tiles) and at the full decode and
+prefill sizes on sampled tokens, within the stated bound around the
 oracle's A4 result."""
 
 import numpy as np
@@ -83,13 +84,17 @@ FWD = [
     # prefill-shaped: several 128-row tiles per expert, ragged tails
     synth.variant(synth.CONFIGS["tiny"], T=400, E=4, k=2, H=1536, I=1024, seed=71, gran=32,
                   act="bf16", global_scale="uniform", routing="zipf"),
-    # decode-shaped batch (A4 always runs on the 128-row tiles)
+    # decode-shaped batch (16-row tiles of the decode kernel)
     synth.variant(synth.CONFIGS["tiny"], T=16, E=32, k=4, H=1024, I=512, seed=72, gran=32,
+                  act="bf16", global_scale="none"),
+    # decode-shaped with K spanning two weight-scale groups (16 chunks of
+    # group32 scales per 128-byte line), the second one ragged
+    synth.variant(synth.CONFIGS["tiny"], T=16, E=8, k=4, H=4608, I=2560, seed=73, gran=32,
                   act="bf16", global_scale="none"),
 ]
 
 
-@pytest.mark.parametrize("cfg", FWD, ids=["prefill", "decode"])
+@pytest.mark.parametrize("cfg", FWD, ids=["prefill", "decode", "decode_long_k"])
 def test_forward_a4(cfg):
     require_gpu()
     print(f"A4 forward: T={cfg.T} E={cfg.E} k={cfg.k} H={cfg.H} I={cfg.I}", flush=True)
@@ -107,6 +112,27 @@ def test_forward_a4(cfg):
     assert torch.equal(f32.view(torch.int32), f32b.view(torch.int32))
     ref, band = _a4_ref(inp, x4, x4sf)
     check_bound(f32.cpu().numpy().astype(np.float64), ref, "A4 forward", band)
+
+
+def test_full_decode_a4_sampled():
+    """The decode32 shape (256 tokens over 256 experts, top-8, H = 6144,
+    I = 2048) with the library quantising x to MXFP4: 16-row expert tiles;
+    the oracle computes a sample of tokens over sampled columns."""
+    require_gpu()
+    cfg = synth.variant(synth.CONFIGS["decode32"], act="bf16")
+    inp = synth.make_moe_inputs(cfg)
+    d = to_dev(inp)
+    print("decode32 A4: running on GPU", flush=True)
+    out = gpu_forward(inp, d, out_dtype=torch.float32, quantize_x="fp4")
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(2)
+    tokens = sorted({0, cfg.T - 1, int(rng.integers(cfg.T)), int(rng.integers(cfg.T))})
+    cols = np.sort(rng.choice(cfg.H, size=768, replace=False))
+    _, x4, x4sf = oracle.quantize_a4(decode_activations(inp.x))
+    print(f"decode32 A4: oracle on tokens {tokens}", flush=True)
+    ref, band = _a4_ref(inp, x4, x4sf, tokens=tokens, out_cols=cols)
+    got = out[tokens][:, torch.from_numpy(cols).cuda()].cpu().numpy().astype(np.float64)
+    check_bound(got, ref, "decode32 A4 sampled", band)
 
 
 def test_full_prefill_a4_sampled():
