@@ -97,6 +97,13 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return u2f(bits1
 __device__ __forceinline__ float swiglu(float g, float u) {
   return g / (1.0f + __expf(-g)) * u;
 }
+// The same with the hardware reciprocal (1 ulp) in place of the IEEE
+// division, for epilogues where SwiGLU is a visible share of the VALU work;
+// the result differs from swiglu() by a few ulp, far below the rounding to
+// FP8 / FP4 that follows.
+__device__ __forceinline__ float swiglu_fast(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
 
 // Smallest e with 448 * 2**e >= a (a > 0 normal): a = M * 2**E, M in [1, 2):
 // 448 = 1.75 * 2**8, so e = E - 8 + (M > 1.75).
