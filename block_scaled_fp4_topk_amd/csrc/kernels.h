@@ -95,7 +95,7 @@ hipError_t launch_fc2_a8(const FcArgs& a, int nt, int max_tiles, hipStream_t s);
 hipError_t launch_fc_decode(const FcArgs& a, int mode, bool fc1, int max_tiles, hipStream_t s);
 
 // Prefill-shaped FP8 x FP4 grouped GEMMs on 128-row expert tiles (direct-
-// to-LDS pipelined, 256 weight rows per workgroup); a4: MXFP4 activations
+// to-LDS pipelined, 512 weight rows per work item); a4: MXFP4 activations
 // (act [rows, K/2], h written as MXFP4).  Needs H % 512 == 0, I % 512 == 0
 // and 32-bit row offsets.
 hipError_t launch_fc_gemm_a8(const FcArgs& a, bool fc1, bool a4, int max_tiles, hipStream_t s);

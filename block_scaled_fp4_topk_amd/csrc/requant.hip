@@ -16,7 +16,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kBlocksPerThread = 4;  // 32-element blocks handled per lane per step
 
-// grid: x = workgroups per expert (grid-stride over the expert's blocks),
+// grid: x = workgroups per expert (a grid stride over the expert's blocks),
 // y = expert.  Each workgroup first tabulates the odd-rounded products of
 // all 256 E4M3 scale bytes with |gs| of its expert.
 __global__ __launch_bounds__(kThreads) void requant_kernel(const uint8_t* src, const uint8_t* src_sf,
@@ -84,10 +84,12 @@ hipError_t launch_requant_g16_g32(const uint8_t* src, const uint8_t* src_sf, con
                                   hipStream_t s) {
   const int64_t nb = N * (K / 32);
   if (nb <= 0 || E <= 0) return hipSuccess;
+  // One step per workgroup (1024 blocks: 16 KB of codes in and out; at most
+  // 2^20 workgroups per expert, N * K / 32 <= 2^30 being checked by the
+  // caller).  On the full layer this ran at 6.0 TB/s, against 5.2 TB/s with
+  // ~32 grid-striding workgroups per CU and 5.8 TB/s with ~256.
   const int64_t per_wg = (int64_t)kThreads * kBlocksPerThread;
-  int64_t gx = (nb + per_wg - 1) / per_wg;
-  const int64_t want = (8192 + E - 1) / E;  // ~32 workgroups per CU over the launch
-  if (gx > want) gx = want;
+  const int64_t gx = (nb + per_wg - 1) / per_wg;
   hipLaunchKernelGGL(requant_kernel, dim3((unsigned)gx, (unsigned)E), dim3(kThreads), 0, s, src,
                      src_sf, gs, dst, dst_sf, (int)nb);
   return hipGetLastError();
