@@ -128,3 +128,24 @@ def test_full_size_sampled(name):
     ref, band = ref_forward(inp, tokens=tokens, out_cols=cols)
     got = out[tokens][:, torch.from_numpy(cols).cuda()].cpu().numpy().astype(np.float64)
     check_bound(got, ref, f"{name} sampled", band)
+
+
+def test_many_items_per_workgroup():
+    """A prefill batch large enough that each persistent GEMM workgroup walks
+    more than one batch of 64 work-item descriptors (FC2: 1536 expert tiles x
+    12 row blocks over one workgroup per CU), checked on sampled tokens."""
+    require_gpu()
+    cfg = synth.variant(synth.CONFIGS["prefill32"], name="prefill_many_items", T=24576, E=32, I=512,
+                        routing="softmax_topk", seed=26, weight_seed=None)
+    inp = synth.make_moe_inputs(cfg)
+    d = to_dev(inp)
+    print(f"many items: T={cfg.T} E={cfg.E} H={cfg.H} I={cfg.I}: running on GPU", flush=True)
+    out = gpu_forward(inp, d, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1)
+    tokens = sorted({0, cfg.T - 1, int(rng.integers(cfg.T)), int(rng.integers(cfg.T))})
+    cols = np.sort(rng.choice(cfg.H, size=768, replace=False))
+    print(f"many items: oracle on tokens {tokens}", flush=True)
+    ref, band = ref_forward(inp, tokens=tokens, out_cols=cols)
+    got = out[tokens][:, torch.from_numpy(cols).cuda()].cpu().numpy().astype(np.float64)
+    check_bound(got, ref, "many items sampled", band)
