@@ -42,9 +42,13 @@ WORKLOAD_TEXT = {
                        "library to E4M3+UE8M0 k32, E2M1 + UE8M0 k32",
     "prefill32_a4": "A4 prefill: T=8192 E=256 top-8 Zipf(1.1) H=6144 I=2048, bf16 x quantised by the "
                     "library to MXFP4 (E2M1+UE8M0 k32), h MXFP4, E2M1 + UE8M0 k32 weights",
+    "prefill32_prep": "prefill: T=8192 E=256 top-8 Zipf(1.1) H=6144 I=2048, E4M3+UE8M0 k32 x, E2M1 + UE8M0 "
+                      "k32 weights in the GEMM layout (moe_fp4_prepare_gemm_weights, not timed)",
+    "prefill32_a4_prep": "A4 prefill: T=8192 E=256 top-8 Zipf(1.1) H=6144 I=2048, bf16 x quantised by the "
+                         "library to MXFP4, h MXFP4, E2M1 + UE8M0 k32 weights in the GEMM layout",
 }
 DTYPE = {"decode16": "f16", "decode32": "fp8xfp4", "decode32_a4": "fp4xfp4", "prefill32": "fp8xfp4", "prefill32_bf16q": "fp8xfp4",
-         "prefill32_a4": "fp4xfp4"}
+         "prefill32_a4": "fp4xfp4", "prefill32_prep": "fp8xfp4", "prefill32_a4_prep": "fp4xfp4"}
 STAGES = ["route", "act_prep", "fc1_swiglu", "fc2", "combine"]
 
 
@@ -68,6 +72,15 @@ class HipEvents:
                                         ctypes.c_void_p(self.arr[j])) != 0:
             raise RuntimeError("hipEventElapsedTime failed")
         return f.value
+
+
+def prepare_weights(moe, torch, d):
+    """Weights of a *_prep workload in the GEMM layout (prepared once, not
+    timed)."""
+    d["w13"], d["w13_sf"] = moe.prepare_gemm_weights(d["w13"], d["w13_sf"], "w13")
+    d["w2"], d["w2_sf"] = moe.prepare_gemm_weights(d["w2"], d["w2_sf"], "w2")
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
 
 
 def to_dev(torch, inp):
@@ -95,12 +108,14 @@ def gpu_forward_into(moe, torch, inp, d, ws, out):
         p = moe.make_problem(c.T, c.E, c.k, c.H, c.I, c.gran,
                              {"fp8": moe.ACT_FP8_UE8M0_K32,
                               "bf16q": moe.ACT_BF16_QUANT_FP8_K32,
-                              "bf16q4": moe.ACT_BF16_QUANT_FP4_K32}.get(c.act, moe.ACT_BF16))
+                              "bf16q4": moe.ACT_BF16_QUANT_FP4_K32}.get(c.act, moe.ACT_BF16),
+                             w_layout="gemm" if c.name.endswith("_prep") else "raw")
         ws = torch.empty(moe.workspace_bytes(p), dtype=torch.uint8, device="cuda")
         out = torch.empty((c.T, c.H), dtype=torch.bfloat16, device="cuda")
     moe.forward(d["x"], d["topk_ids"], d["topk_w"], d["w13"], d["w13_sf"], d["w13_gs"], d["w2"],
                 d["w2_sf"], d["w2_gs"], inp.cfg.gran, x_sf=d["x_sf"], out=out, workspace=ws,
-                quantize_x={"bf16q": "fp8", "bf16q4": "fp4"}.get(inp.cfg.act, False))
+                quantize_x={"bf16q": "fp8", "bf16q4": "fp4"}.get(inp.cfg.act, False),
+                w_layout="gemm" if inp.cfg.name.endswith("_prep") else "raw")
     return ws, out
 
 
@@ -118,7 +133,7 @@ def stage_kernel(cfg, ids, stage):
     nt = (8 if gemm_ok else 4) if active and A / active > 16 else 1
     if nt == 8:
         return (f"fc_gemm_a8_kernel<{'true' if stage == 'fc1_swiglu' else 'false'}, "
-                f"{'true' if a4 else 'false'}>")
+                f"{'true' if a4 else 'false'}, {'true' if cfg.name.endswith('_prep') else 'false'}>")
     if nt == 1:
         return f"fc_decode_kernel<{mode}, {'true' if stage == 'fc1_swiglu' else 'false'}>"
     fc1 = "true" if stage == "fc1_swiglu" else "false"
@@ -131,7 +146,10 @@ def workload_cfg(synth, name):
     if name in synth.CONFIGS:
         return synth.CONFIGS[name]
     base, _, form = name.partition("_")
-    return synth.variant(synth.CONFIGS[base], name=name, act="bf16q4" if form == "a4" else "bf16q")
+    if form == "prep":
+        return synth.variant(synth.CONFIGS[base], name=name)
+    return synth.variant(synth.CONFIGS[base], name=name,
+                         act="bf16q4" if form in ("a4", "a4_prep") else "bf16q")
 
 
 def kernel_file_key(symbol):
@@ -271,6 +289,8 @@ def main():
     print(f"[bench] generating {cfg.name} inputs", file=sys.stderr, flush=True)
     inp = synth.make_moe_inputs(cfg)
     d = to_dev(torch, inp)
+    if cfg.name.endswith("_prep"):
+        prepare_weights(moe, torch, d)
     print("[bench] timing", file=sys.stderr, flush=True)
     ms_step, fwd_ms, stage_ms = run_forward_timed(moe, torch, inp, d, args.steps, args.warmup)
     ab = algorithmic_bytes(cfg, inp.topk_ids)
@@ -363,11 +383,14 @@ def secondary(moe, torch, synth, args, inp16, d16):
                             "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
     del src13, sf13, gs13, src2, sf2, gs2, d13, s13, d2, s2
     torch.cuda.empty_cache()
-    for name in ("decode32", "decode32_a4", "prefill32", "prefill32_bf16q", "prefill32_a4"):
+    for name in ("decode32", "decode32_a4", "prefill32", "prefill32_bf16q", "prefill32_a4", "prefill32_prep",
+                 "prefill32_a4_prep"):
         cfg = workload_cfg(synth, name)
         print(f"[bench] secondary {name}", file=sys.stderr, flush=True)
         inp = synth.make_moe_inputs(cfg)
         d = to_dev(torch, inp)
+        if name.endswith("_prep"):
+            prepare_weights(moe, torch, d)
         steps, warm = (10, 10) if name.startswith("prefill") else (50, 100)
         ms_step, fwd_ms, stage_ms = run_forward_timed(moe, torch, inp, d, steps, warm)
         ab = algorithmic_bytes(cfg, inp.topk_ids)

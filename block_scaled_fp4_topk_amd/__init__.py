@@ -11,6 +11,7 @@ Functions mirror the C entry points:
   route(problem, topk_ids, ...)       -> moe_fp4_route
   forward(x, topk_ids, topk_w, ...)   -> moe_fp4_forward
   requant_gran_k(src, src_sf, ...)    -> fp4_requant_gran_k
+  prepare_gemm_weights(src, src_sf, ...) -> moe_fp4_prepare_gemm_weights
   quantize_act(x, ...)                -> moe_fp4_quantize_act
   quantize_act_fp4(x, ...)            -> moe_fp4_quantize_act_fp4
 """
@@ -21,7 +22,8 @@ import ctypes
 import os
 
 __all__ = ["Problem", "MoeFp4Error", "lib", "workspace_bytes", "route", "forward",
-           "requant_gran_k", "quantize_act", "quantize_act_fp4", "dropped_assignments", "LIB_PATH"]
+           "requant_gran_k", "prepare_gemm_weights", "quantize_act", "quantize_act_fp4",
+           "dropped_assignments", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoefp4.so")
 
@@ -31,11 +33,12 @@ GATE_UP, UP_GATE = 0, 1
 
 
 OUT_BF16, OUT_F32 = 0, 1
+W_RAW, W_GEMM = 0, 1
 
 
 class Problem(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
-                ("T", "E", "top_k", "H", "I", "gran_k", "act_fmt", "w13_order", "out_fmt")]
+                ("T", "E", "top_k", "H", "I", "gran_k", "act_fmt", "w13_order", "out_fmt", "w_layout")]
 
 
 class MoeFp4Error(RuntimeError):
@@ -66,6 +69,9 @@ def lib():
         L.fp4_requant_gran_k.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _P, _P,
                                          ctypes.c_int32, _P, _P, _P, ctypes.c_int32, _P]
         L.fp4_requant_gran_k.restype = st
+        L.moe_fp4_prepare_gemm_weights.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                                   ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P, _P]
+        L.moe_fp4_prepare_gemm_weights.restype = st
         L.moe_fp4_quantize_act.argtypes = [ctypes.c_int64, ctypes.c_int64, _P, _P, _P, _P]
         L.moe_fp4_quantize_act.restype = st
         L.moe_fp4_quantize_act_fp4.argtypes = [ctypes.c_int64, ctypes.c_int64, _P, _P, _P, _P]
@@ -108,11 +114,17 @@ def _dev(t, name, dtypes):
     return t
 
 
-def make_problem(T, E, top_k, H, I, gran_k, act_fmt=ACT_BF16, w13_order=GATE_UP,
-                 out_fmt=OUT_BF16) -> Problem:
+def _order(w13_order):
     if isinstance(w13_order, str):
-        w13_order = {"gate_up": GATE_UP, "w31": GATE_UP, "up_gate": UP_GATE, "w13": UP_GATE}[w13_order]
-    return Problem(T, E, top_k, H, I, gran_k, act_fmt, w13_order, out_fmt)
+        return {"gate_up": GATE_UP, "w31": GATE_UP, "up_gate": UP_GATE, "w13": UP_GATE}[w13_order]
+    return w13_order
+
+
+def make_problem(T, E, top_k, H, I, gran_k, act_fmt=ACT_BF16, w13_order=GATE_UP,
+                 out_fmt=OUT_BF16, w_layout=W_RAW) -> Problem:
+    if isinstance(w_layout, str):
+        w_layout = {"raw": W_RAW, "gemm": W_GEMM}[w_layout]
+    return Problem(T, E, top_k, H, I, gran_k, act_fmt, _order(w13_order), out_fmt, w_layout)
 
 
 def workspace_bytes(problem: Problem) -> int:
@@ -147,14 +159,15 @@ def route(problem: Problem, topk_ids, workspace=None, stream=None):
 
 def forward(x, topk_ids, topk_w, w13, w13_sf, w13_gs, w2, w2_sf, w2_gs, gran_k, x_sf=None,
             w13_order="gate_up", out=None, workspace=None, stream=None, out_dtype=None,
-            quantize_x=False):
+            quantize_x=False, w_layout="raw"):
     """MoE forward on the GPU.  x: [T, H] bfloat16 (A16); uint8/float8_e4m3fn
     [T, H] with x_sf [T, H/32] uint8 (A8); or uint8 [T, H/2] (two E2M1 codes
     per byte) with x_sf (A4).  quantize_x with bfloat16 x asks the library to
     quantise x first: True or "fp8" -> the A8 format (act_fmt
     BF16_QUANT_FP8_K32), "fp4" -> the A4 format (BF16_QUANT_FP4_K32).
-    Weights uint8 as in include/moefp4.h.  Returns out [T, H] bfloat16
-    (default) or float32 (out_dtype=torch.float32)."""
+    Weights uint8 as in include/moefp4.h; w_layout="gemm" for weights from
+    prepare_gemm_weights.  Returns out [T, H] bfloat16 (default) or float32
+    (out_dtype=torch.float32)."""
     import torch
     u8 = (torch.uint8,)
     fp8 = (torch.uint8, torch.float8_e4m3fn)
@@ -186,7 +199,7 @@ def forward(x, topk_ids, topk_w, w13, w13_sf, w13_gs, w2, w2_sf, w2_gs, gran_k, 
     act = (ACT_FP4_UE8M0_K32 if a4 else ACT_FP8_UE8M0_K32 if a8 else
            ACT_BF16_QUANT_FP8_K32 if quant == "fp8" else ACT_BF16_QUANT_FP4_K32 if quant == "fp4" else ACT_BF16)
     p = make_problem(T, E, k, H, two_i // 2, gran_k, act, w13_order,
-                     OUT_F32 if out_dtype == torch.float32 else OUT_BF16)
+                     OUT_F32 if out_dtype == torch.float32 else OUT_BF16, w_layout)
     if out is None:
         out = torch.empty((T, H), dtype=out_dtype, device=x.device)
     _dev(out, "out", (out_dtype,))
@@ -219,6 +232,26 @@ def requant_gran_k(src, src_sf, src_gs=None, src_gran=16, dst_gran=32, dst=None,
     return dst, dst_sf
 
 
+
+
+def prepare_gemm_weights(src, src_sf, which, w13_order="gate_up", dst=None, dst_sf=None, stream=None):
+    """RAW group32 weights (src [E, N, K/2] uint8, src_sf [E, N, K/32] uint8)
+    -> (dst, dst_sf) of the same shapes in the prefill GEMM layout
+    (moe_fp4_prepare_gemm_weights).  which: "w13" (or 0) / "w2" (or 1)."""
+    import torch
+    _dev(src, "src", (torch.uint8,))
+    _dev(src_sf, "src_sf", (torch.uint8,))
+    w = {"w13": 0, "w2": 1}.get(which, which)
+    E, N, kh = src.shape
+    if dst is None:
+        dst = torch.empty_like(src)
+    if dst_sf is None:
+        dst_sf = torch.empty_like(src_sf)
+    _dev(dst, "dst", (torch.uint8,))
+    _dev(dst_sf, "dst_sf", (torch.uint8,))
+    _check(lib().moe_fp4_prepare_gemm_weights(E, N, 2 * kh, w, _order(w13_order), _ptr(src), _ptr(src_sf),
+                                              _ptr(dst), _ptr(dst_sf), _stream(stream)))
+    return dst, dst_sf
 
 
 def quantize_act_fp4(x, x_fp4=None, x_sf=None, stream=None):

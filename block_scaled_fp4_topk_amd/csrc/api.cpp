@@ -64,6 +64,8 @@ moefp4_status check_problem(const moefp4_problem* p) {
     return fail(MOEFP4_EINVAL, "unknown w13_order %d", p->w13_order);
   if (p->out_fmt != MOEFP4_OUT_BF16 && p->out_fmt != MOEFP4_OUT_F32)
     return fail(MOEFP4_EINVAL, "unknown out_fmt %d", p->out_fmt);
+  if (p->w_layout != MOEFP4_W_RAW && p->w_layout != MOEFP4_W_GEMM)
+    return fail(MOEFP4_EINVAL, "unknown w_layout %d", p->w_layout);
   if (p->H % 32 || p->I % 32)
     return fail(MOEFP4_EINVAL, "H and I must be multiples of 32 (K blocks of the scale grid), got H=%d I=%d",
                 p->H, p->I);
@@ -106,6 +108,12 @@ moefp4_status plan(const moefp4_problem* p, Layout* L) {
                        T * H < (1ull << 31) &&
                        A * I < (1ull << 31) && I * H < (1ull << 31);
   L->nt = avg > 16.0 ? (gemm_ok ? 8 : 4) : 1;
+  if (p->w_layout == MOEFP4_W_GEMM && L->nt != 8)
+    return fail(MOEFP4_EUNSUPPORTED,
+                "GEMM-layout weights are read by the prefill GEMM only (FP8 / FP4 activations, group32, H and "
+                "I multiples of 512, more than 16 assignments per active expert); this problem runs on the %s "
+                "tiles: pass RAW weights",
+                L->nt == 1 ? "16-row decode" : "64-row");
   L->tile_m = 16 * L->nt;
   L->max_tiles = (int)(A / L->tile_m + active);
   size_t o = 0;
@@ -273,7 +281,8 @@ moefp4_status moe_fp4_forward(const moefp4_problem* p, const void* x, const uint
     a.h_sf_out = at<uint8_t>(workspace, L.h_sf);
     stage_mark(2, stream);
     st = hip_status(L.nt == 1   ? moefp4::launch_fc_decode(a, L.a4 ? 3 : 2, true, L.max_tiles, stream)
-                    : L.nt == 8 ? moefp4::launch_fc_gemm_a8(a, true, L.a4, L.max_tiles, stream)
+                    : L.nt == 8 ? moefp4::launch_fc_gemm_a8(a, true, L.a4, p->w_layout == MOEFP4_W_GEMM,
+                                                            L.max_tiles, stream)
                         : moefp4::launch_fc1_a8(a, L.nt, L.max_tiles, stream),
                     "fc1");
   } else {
@@ -318,7 +327,8 @@ moefp4_status moe_fp4_forward(const moefp4_problem* p, const void* x, const uint
   a.y_out = at<float>(workspace, L.y);
   const int mode = L.a4 ? 3 : L.a8 ? 2 : (p->gran_k == 16 ? 0 : 1);
   st = hip_status(L.nt == 1   ? moefp4::launch_fc_decode(a, mode, false, L.max_tiles, stream)
-                  : L.nt == 8 ? moefp4::launch_fc_gemm_a8(a, false, L.a4, L.max_tiles, stream)
+                  : L.nt == 8 ? moefp4::launch_fc_gemm_a8(a, false, L.a4, p->w_layout == MOEFP4_W_GEMM,
+                                                          L.max_tiles, stream)
                   : L.a8 ? moefp4::launch_fc2_a8(a, L.nt, L.max_tiles, stream)
                              : moefp4::launch_fc2_a16(a, p->gran_k, L.nt, L.max_tiles, stream),
                   "fc2");
@@ -366,6 +376,38 @@ moefp4_status fp4_requant_gran_k(int64_t E, int64_t N, int64_t K, const uint8_t*
     }
   moefp4_status st = hip_status(
       moefp4::launch_requant_g16_g32(src, src_sf, src_gs, dst, dst_sf, E, N, K, stream), "requant");
+  return st == MOEFP4_OK ? ok() : st;
+}
+
+moefp4_status moe_fp4_prepare_gemm_weights(int64_t E, int64_t N, int64_t K, int32_t which,
+                                           int32_t w13_order, const uint8_t* src, const uint8_t* src_sf,
+                                           uint8_t* dst, uint8_t* dst_sf, hipStream_t stream) {
+  if (E < 0 || N < 0 || K < 0) return fail(MOEFP4_EINVAL, "E, N, K must be >= 0");
+  if (which != 0 && which != 1) return fail(MOEFP4_EINVAL, "which must be 0 (w13) or 1 (w2), got %d", which);
+  if (w13_order != MOEFP4_GATE_UP && w13_order != MOEFP4_UP_GATE)
+    return fail(MOEFP4_EINVAL, "unknown w13_order %d", w13_order);
+  if (N % 512 || K % 512)
+    return fail(MOEFP4_EINVAL, "N and K must be multiples of 512, got N=%lld K=%lld", (long long)N,
+                (long long)K);
+  if (N * K / 32 >= ((int64_t)1 << 31) || E > 65535)
+    return fail(MOEFP4_EUNSUPPORTED, "N*K/32 must be below 2^31 and E <= 65535");
+  const int64_t n = E * N * K;
+  if (n == 0) return ok();
+  if (!src || !src_sf || !dst || !dst_sf)
+    return fail(MOEFP4_EINVAL, "src, src_sf, dst and dst_sf must be non-NULL");
+  if (misaligned(src, 16) || misaligned(dst, 16) || misaligned(src_sf, 16) || misaligned(dst_sf, 16))
+    return fail(MOEFP4_EINVAL, "src, src_sf, dst and dst_sf must be 16-byte aligned");
+  struct R { uintptr_t b, e; } r[4] = {
+      {(uintptr_t)src, (uintptr_t)src + (uintptr_t)(n / 2)},
+      {(uintptr_t)src_sf, (uintptr_t)src_sf + (uintptr_t)(n / 32)},
+      {(uintptr_t)dst, (uintptr_t)dst + (uintptr_t)(n / 2)},
+      {(uintptr_t)dst_sf, (uintptr_t)dst_sf + (uintptr_t)(n / 32)}};
+  for (int i = 0; i < 4; ++i)
+    for (int j = i + 1; j < 4; ++j)
+      if (r[i].b < r[j].e && r[j].b < r[i].e) return fail(MOEFP4_EINVAL, "buffers overlap");
+  moefp4_status st = hip_status(
+      moefp4::launch_prepare_gemm(src, src_sf, dst, dst_sf, E, N, K, which == 0, w13_order, stream),
+      "prepare_gemm_weights");
   return st == MOEFP4_OK ? ok() : st;
 }
 

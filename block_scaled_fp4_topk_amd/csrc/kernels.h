@@ -97,8 +97,15 @@ hipError_t launch_fc_decode(const FcArgs& a, int mode, bool fc1, int max_tiles, 
 // Prefill-shaped FP8 x FP4 grouped GEMMs on 128-row expert tiles (direct-
 // to-LDS pipelined, 512 weight rows per work item); a4: MXFP4 activations
 // (act [rows, K/2], h written as MXFP4).  Needs H % 512 == 0, I % 512 == 0
-// and 32-bit row offsets.
-hipError_t launch_fc_gemm_a8(const FcArgs& a, bool fc1, bool a4, int max_tiles, hipStream_t s);
+// and 32-bit row offsets.  prep: weights in the GEMM layout of
+// launch_prepare_gemm.
+hipError_t launch_fc_gemm_a8(const FcArgs& a, bool fc1, bool a4, bool prep, int max_tiles, hipStream_t s);
+
+// RAW group32 weights [E, N, K/2] + [E, N, K/32] -> the GEMM layout of the
+// prefill kernels (moe_fp4_prepare_gemm_weights); N, K multiples of 512,
+// N * K / 32 < 2^31.
+hipError_t launch_prepare_gemm(const uint8_t* src, const uint8_t* src_sf, uint8_t* dst, uint8_t* dst_sf,
+                               int64_t E, int64_t N, int64_t K, bool w13, int w13_order, hipStream_t s);
 
 // out[t, :] = sum_j w[t, j] * y[slot_of[t*k + j], :]  (f32, or rounded to bf16)
 hipError_t launch_combine(const float* y, const int32_t* slot_of, const float* topk_w, int T,

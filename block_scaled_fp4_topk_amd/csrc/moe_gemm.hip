@@ -160,8 +160,11 @@ __device__ __forceinline__ void lgkm_wait_n() {
 __device__ __forceinline__ void touch(v4i& a) { asm volatile("" : "+v"(a)); }
 
 // A4: MXFP4 activations (E2M1 + UE8M0 per 32, K/2 bytes per row) and h
-// quantised to MXFP4 by FC1; both MFMA operands FP4.
-template <bool FC1, bool A4>
+// quantised to MXFP4 by FC1; both MFMA operands FP4.  PREP: weights in the
+// GEMM layout of moe_fp4_prepare_gemm_weights (each stage of a 512-row block
+// a contiguous 32 KB image of the LDS weight area, each scale group a
+// contiguous 8 KB image of the weight-scale area).
+template <bool FC1, bool A4, bool PREP>
 __global__ __launch_bounds__(256, 1) void fc_gemm_a8_kernel(FcArgs a, int nblk) {
   // load instructions per wave: activations (128 rows x 128 or 64 bytes of
   // a stage over 4 waves) + 8 for weights (512 rows x 64 bytes); per scale
@@ -266,7 +269,8 @@ __global__ __launch_bounds__(256, 1) void fc_gemm_a8_kernel(FcArgs a, int nblk) 
   uint32_t aoff[4], woff0 = 0, wsl = 0, asl = 0;  // (A4 uses aoff[0..1])
   auto set_scale_loads = [&](const Item& it, int mine) __attribute__((always_inline)) {
     wsbase = a.wsf + (size_t)it.e * N * (size_t)(K >> 5);
-    wsl = wrow(it.nb, 128 * wave + lane) * (K >> 5);
+    // (GEMM layout: the row block's groups are 8 KB images of wsc)
+    wsl = PREP ? it.nb * (K >> 9) * 8192 + (128 * wave + lane) * 16 : wrow(it.nb, 128 * wave + lane) * (K >> 5);
     asl = mine * (K >> 5);
   };
   auto set_operand_loads = [&](const Item& it, int mine) __attribute__((always_inline)) {
@@ -284,7 +288,9 @@ __global__ __launch_bounds__(256, 1) void fc_gemm_a8_kernel(FcArgs a, int nblk) 
       }
     }
     const int r = 128 * wave + (lane >> 2), pw = (lane & 3) ^ ((lane >> 4) & 3);
-    woff0 = wrow(it.nb, r) * (K >> 1) + 16 * pw;
+    // (GEMM layout: the row block's stages are 32 KB images of the LDS weight
+    // area, instruction i of wave w its KB 8 w + i)
+    woff0 = PREP ? it.nb * (K >> 7) * 32768 + (512 * wave + lane) * 16 : wrow(it.nb, r) * (K >> 1) + 16 * pw;
   };
   // (uniform 64-bit base + 32-bit lane offset: the scalar-base address form)
   // Load instruction j (0 .. kOps - 1) of a stage: activations first, then
@@ -300,8 +306,8 @@ __global__ __launch_bounds__(256, 1) void fc_gemm_a8_kernel(FcArgs a, int nblk) 
                                          0, 0);
     } else {
       const int i = j - kActOps;
-      __builtin_amdgcn_global_load_lds(wbase + (woff0 + 8 * K * i + (k0 >> 1)),
-                                       &ring.d[st + kW + (512 * wave + 64 * i) * 16], 16, 0, 0);
+      const uint32_t wo = PREP ? woff0 + 1024 * i + 256 * k0 : woff0 + 8 * K * i + (k0 >> 1);
+      __builtin_amdgcn_global_load_lds(wbase + wo, &ring.d[st + kW + (512 * wave + 64 * i) * 16], 16, 0, 0);
     }
   };
   auto issue = [&](uint32_t b, uint32_t k0) __attribute__((always_inline)) {
@@ -309,9 +315,11 @@ __global__ __launch_bounds__(256, 1) void fc_gemm_a8_kernel(FcArgs a, int nblk) 
     for (int j = 0; j < kOps; ++j) issue_one(b, k0, j);
   };
   auto issue_scales = [&](uint32_t kb0) __attribute__((always_inline)) {
-    __builtin_amdgcn_global_load_lds(wsbase + (wsl + kb0), &side.wsc[128 * wave * 16], 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(wsbase + (wsl + 64 * (K >> 5) + kb0), &side.wsc[(128 * wave + 64) * 16], 16,
-                                     0, 0);
+    // (kb0: the group's byte offset in a RAW scale row, 16 per group)
+    const uint32_t w0 = PREP ? wsl + 512 * kb0 : wsl + kb0;
+    const uint32_t w1 = PREP ? w0 + 1024 : w0 + 64 * (K >> 5);
+    __builtin_amdgcn_global_load_lds(wsbase + w0, &side.wsc[128 * wave * 16], 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(wsbase + w1, &side.wsc[(128 * wave + 64) * 16], 16, 0, 0);
     __builtin_amdgcn_global_load_lds(a.act_sf + (asl + kb0), &side.asc[wave][0], 16, 0, 0);
   };
 
@@ -669,7 +677,7 @@ __global__ __launch_bounds__(256, 1) void fc_gemm_a8_kernel(FcArgs a, int nblk) 
   }
 }
 
-template <bool FC1, bool A4>
+template <bool FC1, bool A4, bool PREP>
 hipError_t launch_one(const FcArgs& a, int max_tiles, hipStream_t s) {
   const int nblk = FC1 ? a.I / 256 : a.H / 512;
   if (max_tiles <= 0 || nblk <= 0) return hipSuccess;
@@ -681,15 +689,65 @@ hipError_t launch_one(const FcArgs& a, int max_tiles, hipStream_t s) {
     cus = 256;
   const long long items = (long long)max_tiles * nblk;
   const long long grid = std::min<long long>(cus / 8 * 8, (items + 7) / 8 * 8);
-  hipLaunchKernelGGL((fc_gemm_a8_kernel<FC1, A4>), dim3((unsigned)grid), dim3(256), 0, s, a, nblk);
+  hipLaunchKernelGGL((fc_gemm_a8_kernel<FC1, A4, PREP>), dim3((unsigned)grid), dim3(256), 0, s, a, nblk);
   return hipGetLastError();
+}
+
+// GEMM weight layout (moe_fp4_prepare_gemm_weights): one 16-byte piece per
+// lane, read and written whole.  Codes: piece c of expert e, c = (nb * K/128
+// + s) * 2048 + j; scales: piece c = (nb * K/512 + g) * 512 + i.
+__global__ __launch_bounds__(256) void prepare_gemm_kernel(const uint8_t* __restrict__ src,
+                                                           const uint8_t* __restrict__ src_sf,
+                                                           uint8_t* __restrict__ dst, uint8_t* __restrict__ dst_sf,
+                                                           int N, int K, int w13, int w13_order, int ncode,
+                                                           int nscale) {
+  const int e = blockIdx.y;
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= ncode + nscale) return;
+  // src row of row i of 512-row block nb
+  auto row = [&](int nb, int i) {
+    if (!w13) return nb * 512 + i;
+    const int i0 = nb * 256 + (i & 255);
+    return ((i >= 256) != (w13_order != 0)) ? N / 2 + i0 : i0;
+  };
+  const size_t ecode = (size_t)e * N * (size_t)(K >> 1), escale = (size_t)e * N * (size_t)(K >> 5);
+  if (c < ncode) {
+    const int ns = K >> 7;
+    const int j = c & 2047, bs = c >> 11;  // slot, (block, stage)
+    const int nb = bs / ns, st = bs - nb * ns;
+    const int piece = (j & 3) ^ ((j >> 4) & 3);
+    const uint4 v = *reinterpret_cast<const uint4*>(src + ecode + (size_t)row(nb, j >> 2) * (K >> 1) + 64 * st +
+                                                    16 * piece);
+    *reinterpret_cast<uint4*>(dst + ecode + (size_t)c * 16) = v;
+  } else {
+    const int cs = c - ncode;
+    const int ng = K >> 9;
+    const int i = cs & 511, bg = cs >> 9;  // row, (block, group)
+    const int nb = bg / ng, g = bg - nb * ng;
+    const uint4 v = *reinterpret_cast<const uint4*>(src_sf + escale + (size_t)row(nb, i) * (K >> 5) + 16 * g);
+    *reinterpret_cast<uint4*>(dst_sf + escale + (size_t)cs * 16) = v;
+  }
 }
 
 }  // namespace
 
-hipError_t launch_fc_gemm_a8(const FcArgs& a, bool fc1, bool a4, int max_tiles, hipStream_t s) {
-  if (a4) return fc1 ? launch_one<true, true>(a, max_tiles, s) : launch_one<false, true>(a, max_tiles, s);
-  return fc1 ? launch_one<true, false>(a, max_tiles, s) : launch_one<false, false>(a, max_tiles, s);
+hipError_t launch_fc_gemm_a8(const FcArgs& a, bool fc1, bool a4, bool prep, int max_tiles, hipStream_t s) {
+  if (prep) {
+    if (a4) return fc1 ? launch_one<true, true, true>(a, max_tiles, s) : launch_one<false, true, true>(a, max_tiles, s);
+    return fc1 ? launch_one<true, false, true>(a, max_tiles, s) : launch_one<false, false, true>(a, max_tiles, s);
+  }
+  if (a4) return fc1 ? launch_one<true, true, false>(a, max_tiles, s) : launch_one<false, true, false>(a, max_tiles, s);
+  return fc1 ? launch_one<true, false, false>(a, max_tiles, s) : launch_one<false, false, false>(a, max_tiles, s);
+}
+
+hipError_t launch_prepare_gemm(const uint8_t* src, const uint8_t* src_sf, uint8_t* dst, uint8_t* dst_sf,
+                               int64_t E, int64_t N, int64_t K, bool w13, int w13_order, hipStream_t s) {
+  const int64_t ncode = N * K / 32, nscale = N * K / 512;  // 16-byte pieces per expert
+  if (E <= 0 || ncode <= 0) return hipSuccess;
+  const int64_t gx = (ncode + nscale + 255) / 256;
+  hipLaunchKernelGGL(prepare_gemm_kernel, dim3((unsigned)gx, (unsigned)E), dim3(256), 0, s, src, src_sf, dst, dst_sf,
+                     (int)N, (int)K, w13 ? 1 : 0, w13_order, (int)ncode, (int)nscale);
+  return hipGetLastError();
 }
 
 }  // namespace moefp4

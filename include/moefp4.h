@@ -88,12 +88,24 @@ typedef enum moefp4_w13_order { MOEFP4_GATE_UP = 0, MOEFP4_UP_GATE = 1 } moefp4_
  * (the same value the BF16 output is rounded from). */
 typedef enum moefp4_out_fmt { MOEFP4_OUT_BF16 = 0, MOEFP4_OUT_F32 = 1 } moefp4_out_fmt;
 
+/* Weight layouts.  RAW: the [E, N, K/2] codes and [E, N, K/gran] scales
+ * described at the top (the checkpoint layout of [P3]).  GEMM: the layout
+ * moe_fp4_prepare_gemm_weights writes from RAW group32 weights: the same
+ * bytes ordered as the prefill GEMM stages them, so that it reads every
+ * weight stage with contiguous 1 KB loads.  The layout itself is this
+ * library's (it follows its prefill kernel); the step is the counterpart of
+ * the weight preparation of [P1] (prepare_fp4_weights_for_mega_moe turning
+ * raw grouped FP4 weights and scales into the fused kernel's layouts, the
+ * benchmark feeding both forms from the same raw tensors) and of [P3]
+ * _repack_weight. */
+typedef enum moefp4_w_layout { MOEFP4_W_RAW = 0, MOEFP4_W_GEMM = 1 } moefp4_w_layout;
+
 /* Problem description.  T tokens, E experts, top_k experts per token,
  * H hidden size, I intermediate size (w13 has 2I rows), gran_k 16 or 32,
  * act_fmt (moefp4_act_fmt), w13_order (moefp4_w13_order), out_fmt
- * (moefp4_out_fmt). */
+ * (moefp4_out_fmt), w_layout (moefp4_w_layout) of w13/w13_sf and w2/w2_sf. */
 typedef struct moefp4_problem {
-  int32_t T, E, top_k, H, I, gran_k, act_fmt, w13_order, out_fmt;
+  int32_t T, E, top_k, H, I, gran_k, act_fmt, w13_order, out_fmt, w_layout;
 } moefp4_problem;
 
 /* Workspace size for moe_fp4_route / moe_fp4_forward on problem p.
@@ -140,6 +152,30 @@ moefp4_status moe_fp4_forward(const moefp4_problem* p,
                               const uint8_t* w2, const uint8_t* w2_sf, const float* w2_gs,
                               void* out, void* workspace, size_t ws_bytes,
                               hipStream_t stream);
+
+/* Reorder group32 weights (RAW layout, UE8M0 scales) into the GEMM layout
+ * of the prefill kernels.  which = 0: w13 (N = 2I rows in w13_order, K =
+ * H); which = 1: w2 (N = H, K = I).  The GEMM's weight rows are taken in
+ * blocks of 512: block nb of w13 is gate rows [256 nb, 256 nb + 256) then
+ * the matching up rows (w13_order says where in src they are); block nb of
+ * w2 is rows [512 nb, 512 nb + 512).  With r(nb, i) the src row of the
+ * block's i-th row:
+ *   codes  dst[e][((nb * K/128 + s) * 2048 + j) * 16 + b] =
+ *            src[e][r(nb, j >> 2)][64 s + 16 ((j & 3) ^ ((j >> 4) & 3)) + b]
+ *          for K stage s (128 elements), slot j in [0, 2048), byte b < 16;
+ *   scales dst_sf[e][((nb * K/512 + g) * 512 + i) * 16 + b] =
+ *            src_sf[e][r(nb, i)][16 g + b]   for group g (512 elements).
+ * dst and dst_sf have the sizes of src and src_sf.  Device memory, 16-byte
+ * aligned, disjoint from each other and from src / src_sf (EINVAL
+ * otherwise); N and K multiples of 512 (EINVAL otherwise).  A forward with
+ * w_layout = GEMM reads these buffers where it runs the prefill GEMM (FP8 or
+ * FP4 activations, group32, H and I multiples of 512, more than 16
+ * assignments per active expert on average: T * top_k > 16 * min(T * top_k,
+ * E)) and returns EUNSUPPORTED for other problems. */
+moefp4_status moe_fp4_prepare_gemm_weights(int64_t E, int64_t N, int64_t K, int32_t which,
+                                           int32_t w13_order, const uint8_t* src,
+                                           const uint8_t* src_sf, uint8_t* dst, uint8_t* dst_sf,
+                                           hipStream_t stream);
 
 /* Requantise E x [N, K] FP4 from src_gran to dst_gran ([P2] Requantization
  * path; [P1] requant_fp4_to_gran_k): dequantise with the group16 E4M3 scales

@@ -30,8 +30,8 @@ def L():
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
     assert {"moe_fp4_forward", "moe_fp4_route", "fp4_requant_gran_k", "moe_fp4_workspace_bytes",
-            "moe_fp4_quantize_act", "moe_fp4_quantize_act_fp4", "moefp4_last_error",
-            "moefp4_version"} <= set(names)
+            "moe_fp4_quantize_act", "moe_fp4_quantize_act_fp4", "moe_fp4_prepare_gemm_weights",
+            "moefp4_last_error", "moefp4_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
     assert b"gfx950" in L.moefp4_version()
@@ -42,13 +42,13 @@ def test_binding_exports():
     has its Python wrapper (no GPU needed)."""
     for n in m.__all__:
         assert hasattr(m, n), n
-    for n in ("forward", "route", "requant_gran_k", "quantize_act", "quantize_act_fp4",
-              "workspace_bytes", "dropped_assignments"):
+    for n in ("forward", "route", "requant_gran_k", "prepare_gemm_weights", "quantize_act",
+              "quantize_act_fp4", "workspace_bytes", "dropped_assignments"):
         assert callable(getattr(m, n)), n
 
 
 def P(**kw):
-    d = dict(T=64, E=256, top_k=8, H=6144, I=2048, gran_k=16, act_fmt=0, w13_order=0, out_fmt=0)
+    d = dict(T=64, E=256, top_k=8, H=6144, I=2048, gran_k=16, act_fmt=0, w13_order=0, out_fmt=0, w_layout=0)
     d.update(kw)
     return m.Problem(**d)
 
@@ -87,6 +87,11 @@ def test_workspace_sizes(L):
     (dict(w13_order=3), m.EINVAL),
     (dict(out_fmt=2), m.EINVAL),
     (dict(T=-1), m.EINVAL),
+    (dict(w_layout=2), m.EINVAL),
+    # GEMM-layout weights: only where the prefill GEMM runs
+    (dict(w_layout=1), m.EUNSUPPORTED),                                   # bf16 decode
+    (dict(w_layout=1, gran_k=32, act_fmt=1), m.EUNSUPPORTED),             # FP8 decode (16-row tiles)
+    (dict(w_layout=1, gran_k=32, act_fmt=1, T=8192, I=2304), m.EUNSUPPORTED),  # 64-row tiles
 ])
 def test_problem_validation(L, kw, status):
     st, _ = ws_status(P(**kw))
@@ -164,3 +169,28 @@ def test_forward_quant_x_rejects_x_sf(L):
     z = ctypes.c_void_p(0)
     st = L.moe_fp4_forward(ctypes.byref(p), f, f, f, f, f, f, z, f, f, z, f, f, 1 << 40, z)
     assert st == m.EINVAL and b"x_sf" in L.moefp4_last_error()
+
+
+def test_gemm_layout_problem_accepted(L):
+    st, n = ws_status(P(T=8192, gran_k=32, act_fmt=1, w_layout=1))
+    assert st == 0 and n > 0
+    st, n = ws_status(P(T=8192, gran_k=32, act_fmt=4, w_layout=1))
+    assert st == 0 and n > 0
+
+
+def test_prepare_gemm_rejects_before_launch(L):
+    z = ctypes.c_void_p(0)
+    f = ctypes.c_void_p(1 << 20)
+    g = ctypes.c_void_p(1 << 32)
+    h = ctypes.c_void_p(1 << 34)
+    k = ctypes.c_void_p(1 << 36)
+    pg = L.moe_fp4_prepare_gemm_weights
+    assert pg(2, 1024, 512, 0, 0, z, z, z, z, z) == m.EINVAL             # NULL
+    assert pg(2, 1000, 512, 0, 0, f, g, h, k, z) == m.EINVAL             # N % 512
+    assert pg(2, 1024, 640, 1, 0, f, g, h, k, z) == m.EINVAL             # K % 512
+    assert pg(2, 1024, 512, 2, 0, f, g, h, k, z) == m.EINVAL             # which
+    assert pg(2, 1024, 512, 0, 5, f, g, h, k, z) == m.EINVAL             # order
+    assert pg(2, 1024, 512, 0, 0, f, g, f, k, z) == m.EINVAL             # dst overlaps src
+    assert pg(2, 1024, 512, 0, 0, ctypes.c_void_p((1 << 20) + 4), g, h, k, z) == m.EINVAL  # alignment
+    assert pg(0, 1024, 512, 0, 0, z, z, z, z, z) == 0                    # empty
+    assert len(L.moefp4_last_error()) == 0
