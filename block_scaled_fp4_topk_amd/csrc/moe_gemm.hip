@@ -337,31 +337,36 @@ __global__ __launch_bounds__(256, 1) void fc_gemm_a8_kernel(FcArgs a, int nblk) 
   // group, tile row r16); the row groups' offsets are compile-time
   const uint32_t ws_base = lds_addr(&side.wsc[0]) + (wrow0 + r16) * 16;
   const uint32_t as_base = lds_addr(&side.asc[0][0]) + r16 * 16;
-  auto read_scales = [&](LaneScales& d) __attribute__((always_inline)) {
-    v4i t[8];
+  // A group's scales in two halves: the reads (into 16 line registers), and
+  // the wait and the byte selection.  Between them the reads complete under
+  // other work (the last MFMAs of the group before).
+  struct ScaleLines { v4i t[16]; };
+  auto issue_scale_reads = [&](ScaleLines& L) __attribute__((always_inline)) {
     auto rw = [&](auto rgi) __attribute__((always_inline)) {
       constexpr int rg = decltype(rgi)::value;
-      t[rg] = lds_read16o<16 * roff<FC1>(rg)>(ws_base);
+      L.t[rg] = lds_read16o<16 * roff<FC1>(rg)>(ws_base);
     };
     auto ra = [&](auto tgi) __attribute__((always_inline)) {
       constexpr int tg = decltype(tgi)::value;
       // tile row 16 tg + r16 sits in region (tg >> 1), lane (tg & 1) * 16 + r16
-      t[tg] = lds_read16o<(tg >> 1) * 1024 + (tg & 1) * 256>(as_base);
+      L.t[8 + tg] = lds_read16o<(tg >> 1) * 1024 + (tg & 1) * 256>(as_base);
     };
     static_for<8>(rw);
-    lds_wait(t[0], t[1], t[2], t[3], t[4], t[5], t[6], t[7]);
+    static_for<8>(ra);
+  };
+  auto finish_scales = [&](ScaleLines& L, LaneScales& d) __attribute__((always_inline)) {
+    lds_wait(L.t[0], L.t[1], L.t[2], L.t[3], L.t[4], L.t[5], L.t[6], L.t[7]);
+    lds_wait(L.t[8], L.t[9], L.t[10], L.t[11], L.t[12], L.t[13], L.t[14], L.t[15]);
     // (the empty asm statements keep the byte selection here: sunk to the
     // MFMAs, it would keep all 16 lines alive through the group)
 #pragma unroll
     for (int rg = 0; rg < 8; ++rg) {
-      d.w[rg] = lane_bytes(t[rg]);
+      d.w[rg] = lane_bytes(L.t[rg]);
       asm volatile("" : "+v"(d.w[rg]));
     }
-    static_for<8>(ra);
-    lds_wait(t[0], t[1], t[2], t[3], t[4], t[5], t[6], t[7]);
 #pragma unroll
     for (int tg = 0; tg < 8; ++tg) {
-      d.a[tg] = lane_bytes(t[tg]);
+      d.a[tg] = lane_bytes(L.t[8 + tg]);
       asm volatile("" : "+v"(d.a[tg]));
     }
   };
@@ -396,7 +401,8 @@ __global__ __launch_bounds__(256, 1) void fc_gemm_a8_kernel(FcArgs a, int nblk) 
   // activation fragments are read.  hook(j), j = 0..15, runs after every 4
   // MFMA slots (it issues the loads of a later stage).
   constexpr int NX = A4 ? 1 : 2;  // LDS reads per activation fragment
-  auto compute = [&](uint32_t b, const LaneScales& g, int nv, auto&& hook) __attribute__((always_inline)) {
+  auto compute = [&](uint32_t b, const LaneScales& g, int nv, auto&& hook, auto&& before_last)
+      __attribute__((always_inline)) {
     const uint32_t sb = lds_addr(&ring.d[0]) + b * kStage;
     const uint32_t bw = sb + kW + 64 * wrow0 + lw;       // weight row group 0's fragment
     const uint32_t bx0 = sb + (A4 ? lw : la0);           // token group 0's fragment (FP8: first half)
@@ -483,6 +489,8 @@ __global__ __launch_bounds__(256, 1) void fc_gemm_a8_kernel(FcArgs a, int nblk) 
       if constexpr (pr < 3) {
         read_x(std::integral_constant<int, 2 * pr + 2>{});
         read_x(std::integral_constant<int, 2 * pr + 3>{});
+      } else {
+        before_last();
       }
       __builtin_amdgcn_sched_barrier(0);
       group(std::integral_constant<int, 2 * pr>{}, none);
@@ -608,6 +616,7 @@ __global__ __launch_bounds__(256, 1) void fc_gemm_a8_kernel(FcArgs a, int nblk) 
   uint32_t bcur = 0;  // ring buffer of the stage being multiplied
 
   LaneScales gcur;
+  bool first = true;
   int cs = 0;        // stage of the current item
   int next_mine = 0; // the next item's source row of tile row 32 w + (lane & 31)
   for (;;) {
@@ -625,7 +634,14 @@ __global__ __launch_bounds__(256, 1) void fc_gemm_a8_kernel(FcArgs a, int nblk) 
       WAIT_VM(kOps + kScaleOps);
     }
     barrier();
-    if (P == 0) read_scales(gcur);
+    // (a group's scales are read at the previous group's last step; the
+    // first group's here)
+    if (first) {
+      ScaleLines l0;
+      issue_scale_reads(l0);
+      finish_scales(l0, gcur);
+      first = false;
+    }
     if (P == 1) {
       if (!last_group) {
         issue_scales((cs - 1 + GS) * 4);
@@ -651,15 +667,23 @@ __global__ __launch_bounds__(256, 1) void fc_gemm_a8_kernel(FcArgs a, int nblk) 
     // draining waits cover them)
     const uint32_t bnext = bcur == 0 ? 2 : bcur - 1;  // (bcur + 2) % 3
     const uint32_t k2 = cs + 2 < ns ? (cs + 2) * GK : (cs + 2 - ns) * GK;
+    // at a group's last step the next group's scales (landed with the next
+    // stage) are read under the last MFMAs
+    const bool next_scales = P == GS - 1 && (!last_group || has_next);
+    ScaleLines sl;
     compute(bcur, gcur, cur.ne - cur.m0, [&](int j) __attribute__((always_inline)) {
       if (j < kOps) issue_one(bnext, k2, j);
+    }, [&]() __attribute__((always_inline)) {
+      if (next_scales) issue_scale_reads(sl);
     });
-    // the next stage's scale bytes to the low byte of each word
+    // the next stage's scale bytes to the low byte of each word (or the
+    // next group's words)
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       gcur.w[i] >>= 8;
       gcur.a[i] >>= 8;
     }
+    if (next_scales) finish_scales(sl, gcur);
     bcur = bcur == 2 ? 0 : bcur + 1;
     if (++cs < ns) continue;
     epilogue(cur);
