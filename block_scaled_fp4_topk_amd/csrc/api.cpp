@@ -17,9 +17,6 @@ namespace {
 thread_local std::string g_err;
 thread_local hipEvent_t* g_stage_events = nullptr;
 
-void stage_mark(int i, hipStream_t s) {
-  if (g_stage_events) hipEventRecord(g_stage_events[i], s);
-}
 
 moefp4_status fail(moefp4_status st, const char* fmt, ...) {
   char buf[512];
@@ -156,6 +153,12 @@ moefp4_status hip_status(hipError_t e, const char* what) {
   return MOEFP4_OK;
 }
 
+// stage boundary events of moefp4_set_stage_events (timing only)
+moefp4_status stage_mark(int i, hipStream_t s) {
+  return g_stage_events ? hip_status(hipEventRecord(g_stage_events[i], s), "stage event")
+                        : MOEFP4_OK;
+}
+
 moefp4_status route_into(const moefp4_problem* p, const Layout& L, const int32_t* ids,
                          int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* slot_of,
                          void* ws, uint32_t* zero_words, int n_zero, const void* x, float* row_scale,
@@ -241,7 +244,7 @@ moefp4_status moe_fp4_forward(const moefp4_problem* p, const void* x, const uint
   int32_t* sorted = at<int32_t>(workspace, L.sorted);
   int32_t* slot_of = at<int32_t>(workspace, L.slot_of);
   uint32_t* hmax = L.g16_a16 ? at<uint32_t>(workspace, L.hmax) : nullptr;
-  stage_mark(0, stream);
+  if ((st = stage_mark(0, stream)) != MOEFP4_OK) return st;
   // group16 weights with bf16 x on 16-row tiles: the route launch also
   // computes the per-token fp16 staging scales, and FC1 converts while staging
   const bool stage_f16 = L.g16_a16 && L.nt == 1;
@@ -254,7 +257,7 @@ moefp4_status moe_fp4_forward(const moefp4_problem* p, const void* x, const uint
                   L.g16_a16 ? A : 0, (stage_f16 || L.quant_x) ? x : nullptr,
                   stage_f16 ? xs : nullptr, x8, x8_sf, stream);
   if (st != MOEFP4_OK) return st;
-  stage_mark(1, stream);
+  if ((st = stage_mark(1, stream)) != MOEFP4_OK) return st;
 
   moefp4::FcArgs a;
   memset(&a, 0, sizeof a);
@@ -279,7 +282,7 @@ moefp4_status moe_fp4_forward(const moefp4_problem* p, const void* x, const uint
     a.act = L.quant_x ? x8 : x;
     a.act_sf = L.quant_x ? x8_sf : x_sf;
     a.h_sf_out = at<uint8_t>(workspace, L.h_sf);
-    stage_mark(2, stream);
+    if ((st = stage_mark(2, stream)) != MOEFP4_OK) return st;
     st = hip_status(L.nt == 1   ? moefp4::launch_fc_decode(a, L.a4 ? 3 : 2, true, L.max_tiles, stream)
                     : L.nt == 8 ? moefp4::launch_fc_gemm_a8(a, true, L.a4, p->w_layout == MOEFP4_W_GEMM,
                                                             L.max_tiles, stream)
@@ -302,14 +305,14 @@ moefp4_status moe_fp4_forward(const moefp4_problem* p, const void* x, const uint
     } else {
       a.act = x;
     }
-    stage_mark(2, stream);
+    if ((st = stage_mark(2, stream)) != MOEFP4_OK) return st;
     st = hip_status(L.nt == 1
                         ? moefp4::launch_fc_decode(a, p->gran_k == 16 ? 0 : 1, true, L.max_tiles, stream)
                         : moefp4::launch_fc1_a16(a, p->gran_k, L.nt, L.max_tiles, stream),
                     "fc1");
   }
   if (st != MOEFP4_OK) return st;
-  stage_mark(3, stream);
+  if ((st = stage_mark(3, stream)) != MOEFP4_OK) return st;
 
   // FC2
   a.w = w2;
@@ -333,13 +336,13 @@ moefp4_status moe_fp4_forward(const moefp4_problem* p, const void* x, const uint
                              : moefp4::launch_fc2_a16(a, p->gran_k, L.nt, L.max_tiles, stream),
                   "fc2");
   if (st != MOEFP4_OK) return st;
-  stage_mark(4, stream);
+  if ((st = stage_mark(4, stream)) != MOEFP4_OK) return st;
 
   st = hip_status(moefp4::launch_combine(a.y_out, slot_of, topk_w, p->T, p->top_k, p->H, out,
                                          p->out_fmt == MOEFP4_OUT_F32, stream),
                   "combine");
   if (st != MOEFP4_OK) return st;
-  stage_mark(5, stream);
+  if ((st = stage_mark(5, stream)) != MOEFP4_OK) return st;
   return ok();
 }
 
