@@ -270,6 +270,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile", action="store_true",
                     help="only the primary workload (for rocprofv3 runs)")
+    ap.add_argument("--requant-only", action="store_true",
+                    help="only the group16 -> group32 requantisation of the decode16 layer "
+                         "(for rocprofv3 runs)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -284,6 +287,15 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     moe.lib()  # fails loudly if the HIP library is not built
+
+    if args.requant_only:
+        print("[bench] generating decode16 weights", file=sys.stderr, flush=True)
+        inp16 = synth.make_moe_inputs(workload_cfg(synth, "decode16"))
+        print("[bench] timing requant", file=sys.stderr, flush=True)
+        res = {"requant_layer": requant_layer(moe, torch, inp16)}
+        res["copy_calibration_bytes"] = copy_calibration(torch)
+        print(json.dumps(res), flush=True)
+        return
 
     cfg = workload_cfg(synth, args.workload)
     print(f"[bench] generating {cfg.name} inputs", file=sys.stderr, flush=True)
@@ -328,14 +340,7 @@ def main():
                     "tflops": flops(cfg) / (ms_step * 1e-3) / 1e12},
     }
     if args.profile:
-        # plain copy of a known size, for scaling the HBM byte counters
-        # (FETCH_SIZE / WRITE_SIZE) of the profiled kernels
-        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-        b = torch.empty_like(a)
-        for _ in range(3):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        res["copy_calibration_bytes"] = 1 << 30
+        res["copy_calibration_bytes"] = copy_calibration(torch)
     if not args.no_cpu_baseline and not args.profile:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(inp)
@@ -344,12 +349,20 @@ def main():
     print(json.dumps(res), flush=True)
 
 
-def secondary(moe, torch, synth, args, inp16, d16):
-    """The other workloads of the hot path, each timed the same way."""
-    out = {}
-    del d16
-    torch.cuda.empty_cache()
-    # group16 -> group32 requantisation of the whole decode16 layer (its weights)
+def copy_calibration(torch):
+    """A plain device copy of 1 GiB, for scaling the HBM byte counters
+    (FETCH_SIZE / WRITE_SIZE) of profiled kernels; returns its size."""
+    a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    return 1 << 30
+
+
+def requant_layer(moe, torch, inp16):
+    """group16 -> group32 requantisation of the whole decode16 layer (its
+    w13 and w2), timed with HIP events over 5 passes after 2 untimed ones."""
     src13 = torch.from_numpy(inp16.w13).cuda()
     sf13 = torch.from_numpy(inp16.w13_sf).cuda()
     gs13 = torch.from_numpy(inp16.w13_gs).cuda()
@@ -377,12 +390,21 @@ def secondary(moe, torch, synth, args, inp16, d16):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / n
     nbytes = sum(int(t.numel()) for t in (src13, sf13, d13, s13, src2, sf2, d2, s2)) + 2 * 256 * 4
-    out["requant_layer"] = {"workload": "requant w13 [256,4096,6144] + w2 [256,6144,2048] g16 -> g32",
-                            "ms": ms, "algorithmic_bytes": nbytes,
-                            "achieved_GBps": nbytes / (ms * 1e-3) / 1e9,
-                            "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    res = {"workload": "requant w13 [256,4096,6144] + w2 [256,6144,2048] g16 -> g32",
+           "ms": ms, "algorithmic_bytes": nbytes,
+           "achieved_GBps": nbytes / (ms * 1e-3) / 1e9,
+           "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
     del src13, sf13, gs13, src2, sf2, gs2, d13, s13, d2, s2
     torch.cuda.empty_cache()
+    return res
+
+
+def secondary(moe, torch, synth, args, inp16, d16):
+    """The other workloads of the hot path, each timed the same way."""
+    out = {}
+    del d16
+    torch.cuda.empty_cache()
+    out["requant_layer"] = requant_layer(moe, torch, inp16)
     for name in ("decode32", "decode32_a4", "prefill32", "prefill32_bf16q", "prefill32_a4", "prefill32_prep",
                  "prefill32_a4_prep"):
         cfg = workload_cfg(synth, name)
