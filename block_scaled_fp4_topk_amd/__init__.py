@@ -8,10 +8,12 @@ present the calls raise.
 
 Functions mirror the C entry points:
   workspace_bytes(problem)            -> moe_fp4_workspace_bytes
+  workspace_offsets(problem)          -> moe_fp4_workspace_offsets
   route(problem, topk_ids, ...)       -> moe_fp4_route
   forward(x, topk_ids, topk_w, ...)   -> moe_fp4_forward
   requant_gran_k(src, src_sf, ...)    -> fp4_requant_gran_k
   prepare_gemm_weights(src, src_sf, ...) -> moe_fp4_prepare_gemm_weights
+  prepare_gemm_weights_g16(src, src_sf, src_gs, ...) -> moe_fp4_prepare_gemm_weights_g16
   quantize_act(x, ...)                -> moe_fp4_quantize_act
   quantize_act_fp4(x, ...)            -> moe_fp4_quantize_act_fp4
 """
@@ -21,8 +23,9 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["Problem", "MoeFp4Error", "lib", "workspace_bytes", "route", "forward",
-           "requant_gran_k", "prepare_gemm_weights", "quantize_act", "quantize_act_fp4",
+__all__ = ["Problem", "MoeFp4Error", "lib", "workspace_bytes", "workspace_offsets", "route", "forward",
+           "forward_problem",
+           "requant_gran_k", "prepare_gemm_weights", "prepare_gemm_weights_g16", "quantize_act", "quantize_act_fp4",
            "dropped_assignments", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoefp4.so")
@@ -61,6 +64,9 @@ def lib():
         st = ctypes.c_int
         L.moe_fp4_workspace_bytes.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(ctypes.c_size_t)]
         L.moe_fp4_workspace_bytes.restype = st
+        L.moe_fp4_workspace_offsets.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(ctypes.c_size_t),
+                                                ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]
+        L.moe_fp4_workspace_offsets.restype = st
         L.moe_fp4_route.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.moe_fp4_route.restype = st
         L.moe_fp4_forward.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
@@ -72,6 +78,9 @@ def lib():
         L.moe_fp4_prepare_gemm_weights.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                                    ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P, _P]
         L.moe_fp4_prepare_gemm_weights.restype = st
+        L.moe_fp4_prepare_gemm_weights_g16.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                                       ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P, _P, _P]
+        L.moe_fp4_prepare_gemm_weights_g16.restype = st
         L.moe_fp4_quantize_act.argtypes = [ctypes.c_int64, ctypes.c_int64, _P, _P, _P, _P]
         L.moe_fp4_quantize_act.restype = st
         L.moe_fp4_quantize_act_fp4.argtypes = [ctypes.c_int64, ctypes.c_int64, _P, _P, _P, _P]
@@ -133,6 +142,16 @@ def workspace_bytes(problem: Problem) -> int:
     return n.value
 
 
+def workspace_offsets(problem: Problem):
+    """(h, h_sf, slot_of) byte offsets of the forward's intermediate h, its
+    UE8M0 scales (0 if none) and the assignment -> slot map in the workspace
+    (moe_fp4_workspace_offsets)."""
+    h, hs, so = ctypes.c_size_t(0), ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check(lib().moe_fp4_workspace_offsets(ctypes.byref(problem), ctypes.byref(h), ctypes.byref(hs),
+                                           ctypes.byref(so)))
+    return h.value, hs.value, so.value
+
+
 def _workspace(problem, workspace, device):
     import torch
     need = workspace_bytes(problem)
@@ -157,6 +176,35 @@ def route(problem: Problem, topk_ids, workspace=None, stream=None):
     return counts, offsets, sa[:A], so[:A]
 
 
+def forward_problem(x, topk_ids, w13, w2, gran_k, x_sf=None, w13_order="gate_up", out_dtype=None,
+                    quantize_x=False, w_layout="raw") -> Problem:
+    """The problem descriptor forward() passes to moe_fp4_forward for these
+    arguments (shapes from the tensors, the activation format from x / x_sf
+    / quantize_x)."""
+    import torch
+    quant = {False: None, None: None, True: "fp8", "fp8": "fp8", "fp4": "fp4"}.get(quantize_x, "?")
+    if quant == "?":
+        raise ValueError(f"quantize_x must be False, True, 'fp8' or 'fp4', got {quantize_x!r}")
+    a8 = x_sf is not None
+    E, two_i, _ = w13.shape
+    H = w2.shape[1]
+    T, xcols = x.shape
+    a4 = a8 and xcols * 2 == H
+    if xcols != H and not a4:
+        raise ValueError(f"x has {xcols} columns; expected H={H} (or H/2 packed FP4 codes with x_sf)")
+    k = topk_ids.shape[1]
+    if out_dtype is None:
+        out_dtype = torch.bfloat16
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out_dtype must be torch.bfloat16 or torch.float32")
+    if quant and a8:
+        raise ValueError("quantize_x takes bfloat16 x without x_sf")
+    act = (ACT_FP4_UE8M0_K32 if a4 else ACT_FP8_UE8M0_K32 if a8 else
+           ACT_BF16_QUANT_FP8_K32 if quant == "fp8" else ACT_BF16_QUANT_FP4_K32 if quant == "fp4" else ACT_BF16)
+    return make_problem(T, E, k, H, two_i // 2, gran_k, act, w13_order,
+                        OUT_F32 if out_dtype == torch.float32 else OUT_BF16, w_layout)
+
+
 def forward(x, topk_ids, topk_w, w13, w13_sf, w13_gs, w2, w2_sf, w2_gs, gran_k, x_sf=None,
             w13_order="gate_up", out=None, workspace=None, stream=None, out_dtype=None,
             quantize_x=False, w_layout="raw"):
@@ -171,9 +219,6 @@ def forward(x, topk_ids, topk_w, w13, w13_sf, w13_gs, w2, w2_sf, w2_gs, gran_k, 
     import torch
     u8 = (torch.uint8,)
     fp8 = (torch.uint8, torch.float8_e4m3fn)
-    quant = {False: None, None: None, True: "fp8", "fp8": "fp8", "fp4": "fp4"}.get(quantize_x, "?")
-    if quant == "?":
-        raise ValueError(f"quantize_x must be False, True, 'fp8' or 'fp4', got {quantize_x!r}")
     a8 = x_sf is not None
     _dev(x, "x", fp8 if a8 else (torch.bfloat16, torch.int16, torch.uint16))
     _dev(x_sf, "x_sf", u8)
@@ -183,25 +228,11 @@ def forward(x, topk_ids, topk_w, w13, w13_sf, w13_gs, w2, w2_sf, w2_gs, gran_k, 
         _dev(t, n, u8)
     _dev(w13_gs, "w13_gs", (torch.float32,))
     _dev(w2_gs, "w2_gs", (torch.float32,))
-    E, two_i, _ = w13.shape
-    H = w2.shape[1]
-    T, xcols = x.shape
-    a4 = a8 and xcols * 2 == H
-    if xcols != H and not a4:
-        raise ValueError(f"x has {xcols} columns; expected H={H} (or H/2 packed FP4 codes with x_sf)")
-    k = topk_ids.shape[1]
     if out_dtype is None:
         out_dtype = torch.bfloat16 if out is None else out.dtype
-    if out_dtype not in (torch.bfloat16, torch.float32):
-        raise TypeError("out_dtype must be torch.bfloat16 or torch.float32")
-    if quant and a8:
-        raise ValueError("quantize_x takes bfloat16 x without x_sf")
-    act = (ACT_FP4_UE8M0_K32 if a4 else ACT_FP8_UE8M0_K32 if a8 else
-           ACT_BF16_QUANT_FP8_K32 if quant == "fp8" else ACT_BF16_QUANT_FP4_K32 if quant == "fp4" else ACT_BF16)
-    p = make_problem(T, E, k, H, two_i // 2, gran_k, act, w13_order,
-                     OUT_F32 if out_dtype == torch.float32 else OUT_BF16, w_layout)
+    p = forward_problem(x, topk_ids, w13, w2, gran_k, x_sf, w13_order, out_dtype, quantize_x, w_layout)
     if out is None:
-        out = torch.empty((T, H), dtype=out_dtype, device=x.device)
+        out = torch.empty((p.T, p.H), dtype=out_dtype, device=x.device)
     _dev(out, "out", (out_dtype,))
     ws = _workspace(p, workspace, x.device)
     _check(lib().moe_fp4_forward(ctypes.byref(p), _ptr(x), _ptr(x_sf), _ptr(topk_ids), _ptr(topk_w),
@@ -251,6 +282,29 @@ def prepare_gemm_weights(src, src_sf, which, w13_order="gate_up", dst=None, dst_
     _dev(dst_sf, "dst_sf", (torch.uint8,))
     _check(lib().moe_fp4_prepare_gemm_weights(E, N, 2 * kh, w, _order(w13_order), _ptr(src), _ptr(src_sf),
                                               _ptr(dst), _ptr(dst_sf), _stream(stream)))
+    return dst, dst_sf
+
+
+def prepare_gemm_weights_g16(src, src_sf, src_gs, which, w13_order="gate_up", dst=None, dst_sf=None,
+                             stream=None):
+    """RAW group16 weights (src [E, N, K/2] uint8, src_sf [E, N, K/16] E4M3
+    bytes, src_gs [E] float32 or None) -> (dst [E, N, K/2], dst_sf [E, N,
+    K/32]) in the prefill GEMM layout with group32 UE8M0 scales, the global
+    scale folded in (moe_fp4_prepare_gemm_weights_g16)."""
+    import torch
+    _dev(src, "src", (torch.uint8,))
+    _dev(src_sf, "src_sf", (torch.uint8,))
+    _dev(src_gs, "src_gs", (torch.float32,))
+    w = {"w13": 0, "w2": 1}.get(which, which)
+    E, N, kh = src.shape
+    if dst is None:
+        dst = torch.empty_like(src)
+    if dst_sf is None:
+        dst_sf = torch.empty((E, N, 2 * kh // 32), dtype=torch.uint8, device=src.device)
+    _dev(dst, "dst", (torch.uint8,))
+    _dev(dst_sf, "dst_sf", (torch.uint8,))
+    _check(lib().moe_fp4_prepare_gemm_weights_g16(E, N, 2 * kh, w, _order(w13_order), _ptr(src), _ptr(src_sf),
+                                                  _ptr(src_gs), _ptr(dst), _ptr(dst_sf), _stream(stream)))
     return dst, dst_sf
 
 

@@ -199,6 +199,17 @@ moefp4_status moe_fp4_workspace_bytes(const moefp4_problem* p, size_t* bytes) {
   return ok();
 }
 
+moefp4_status moe_fp4_workspace_offsets(const moefp4_problem* p, size_t* h, size_t* h_sf, size_t* slot_of) {
+  if (!h || !h_sf || !slot_of) return fail(MOEFP4_EINVAL, "h, h_sf and slot_of must be non-NULL");
+  Layout L;
+  moefp4_status st = plan(p, &L);
+  if (st != MOEFP4_OK) return st;
+  *h = L.h;
+  *h_sf = L.a8 ? L.h_sf : 0;
+  *slot_of = L.slot_of;
+  return ok();
+}
+
 moefp4_status moe_fp4_route(const moefp4_problem* p, const int32_t* topk_ids, int32_t* counts,
                             int32_t* offsets, int32_t* sorted_assign, int32_t* slot_of,
                             void* workspace, size_t ws_bytes, hipStream_t stream) {
@@ -286,7 +297,7 @@ moefp4_status moe_fp4_forward(const moefp4_problem* p, const void* x, const uint
     st = hip_status(L.nt == 1   ? moefp4::launch_fc_decode(a, L.a4 ? 3 : 2, true, L.max_tiles, stream)
                     : L.nt == 8 ? moefp4::launch_fc_gemm_a8(a, true, L.a4, p->w_layout == MOEFP4_W_GEMM,
                                                             L.max_tiles, stream)
-                        : moefp4::launch_fc1_a8(a, L.nt, L.max_tiles, stream),
+                        : moefp4::launch_fc1_a8(a, L.max_tiles, stream),
                     "fc1");
   } else {
     if (stage_f16) {
@@ -308,7 +319,7 @@ moefp4_status moe_fp4_forward(const moefp4_problem* p, const void* x, const uint
     if ((st = stage_mark(2, stream)) != MOEFP4_OK) return st;
     st = hip_status(L.nt == 1
                         ? moefp4::launch_fc_decode(a, p->gran_k == 16 ? 0 : 1, true, L.max_tiles, stream)
-                        : moefp4::launch_fc1_a16(a, p->gran_k, L.nt, L.max_tiles, stream),
+                        : moefp4::launch_fc1_a16(a, p->gran_k, L.max_tiles, stream),
                     "fc1");
   }
   if (st != MOEFP4_OK) return st;
@@ -332,8 +343,8 @@ moefp4_status moe_fp4_forward(const moefp4_problem* p, const void* x, const uint
   st = hip_status(L.nt == 1   ? moefp4::launch_fc_decode(a, mode, false, L.max_tiles, stream)
                   : L.nt == 8 ? moefp4::launch_fc_gemm_a8(a, false, L.a4, p->w_layout == MOEFP4_W_GEMM,
                                                           L.max_tiles, stream)
-                  : L.a8 ? moefp4::launch_fc2_a8(a, L.nt, L.max_tiles, stream)
-                             : moefp4::launch_fc2_a16(a, p->gran_k, L.nt, L.max_tiles, stream),
+                  : L.a8 ? moefp4::launch_fc2_a8(a, L.max_tiles, stream)
+                             : moefp4::launch_fc2_a16(a, p->gran_k, L.max_tiles, stream),
                   "fc2");
   if (st != MOEFP4_OK) return st;
   if ((st = stage_mark(4, stream)) != MOEFP4_OK) return st;
@@ -411,6 +422,39 @@ moefp4_status moe_fp4_prepare_gemm_weights(int64_t E, int64_t N, int64_t K, int3
   moefp4_status st = hip_status(
       moefp4::launch_prepare_gemm(src, src_sf, dst, dst_sf, E, N, K, which == 0, w13_order, stream),
       "prepare_gemm_weights");
+  return st == MOEFP4_OK ? ok() : st;
+}
+
+moefp4_status moe_fp4_prepare_gemm_weights_g16(int64_t E, int64_t N, int64_t K, int32_t which,
+                                               int32_t w13_order, const uint8_t* src, const uint8_t* src_sf,
+                                               const float* src_gs, uint8_t* dst, uint8_t* dst_sf,
+                                               hipStream_t stream) {
+  if (E < 0 || N < 0 || K < 0) return fail(MOEFP4_EINVAL, "E, N, K must be >= 0");
+  if (which != 0 && which != 1) return fail(MOEFP4_EINVAL, "which must be 0 (w13) or 1 (w2), got %d", which);
+  if (w13_order != MOEFP4_GATE_UP && w13_order != MOEFP4_UP_GATE)
+    return fail(MOEFP4_EINVAL, "unknown w13_order %d", w13_order);
+  if (N % 512 || K % 512)
+    return fail(MOEFP4_EINVAL, "N and K must be multiples of 512, got N=%lld K=%lld", (long long)N,
+                (long long)K);
+  if (N * K / 32 >= ((int64_t)1 << 31) || E > 65535)
+    return fail(MOEFP4_EUNSUPPORTED, "N*K/32 must be below 2^31 and E <= 65535");
+  const int64_t n = E * N * K;
+  if (n == 0) return ok();
+  if (!src || !src_sf || !dst || !dst_sf)
+    return fail(MOEFP4_EINVAL, "src, src_sf, dst and dst_sf must be non-NULL");
+  if (misaligned(src, 16) || misaligned(dst, 16) || misaligned(src_sf, 16) || misaligned(dst_sf, 16))
+    return fail(MOEFP4_EINVAL, "src, src_sf, dst and dst_sf must be 16-byte aligned");
+  struct R { uintptr_t b, e; } r[4] = {
+      {(uintptr_t)src, (uintptr_t)src + (uintptr_t)(n / 2)},
+      {(uintptr_t)src_sf, (uintptr_t)src_sf + (uintptr_t)(n / 16)},
+      {(uintptr_t)dst, (uintptr_t)dst + (uintptr_t)(n / 2)},
+      {(uintptr_t)dst_sf, (uintptr_t)dst_sf + (uintptr_t)(n / 32)}};
+  for (int i = 0; i < 4; ++i)
+    for (int j = i + 1; j < 4; ++j)
+      if (r[i].b < r[j].e && r[j].b < r[i].e) return fail(MOEFP4_EINVAL, "buffers overlap");
+  moefp4_status st = hip_status(moefp4::launch_requant_prepare_gemm(src, src_sf, src_gs, dst, dst_sf, E, N, K,
+                                                                    which == 0, w13_order, stream),
+                                "prepare_gemm_weights_g16");
   return st == MOEFP4_OK ? ok() : st;
 }
 

@@ -83,10 +83,12 @@ struct FcArgs {
   float* y_out;              // FC2: [A, H]
 };
 
-hipError_t launch_fc1_a16(const FcArgs& a, int gran, int nt, int max_tiles, hipStream_t s);
-hipError_t launch_fc2_a16(const FcArgs& a, int gran, int nt, int max_tiles, hipStream_t s);
-hipError_t launch_fc1_a8(const FcArgs& a, int nt, int max_tiles, hipStream_t s);
-hipError_t launch_fc2_a8(const FcArgs& a, int nt, int max_tiles, hipStream_t s);
+// 64-row expert tiles (bf16 activations with more than 16 assignments per
+// active expert, and FP8 activations at shapes the prefill GEMM does not take)
+hipError_t launch_fc1_a16(const FcArgs& a, int gran, int max_tiles, hipStream_t s);
+hipError_t launch_fc2_a16(const FcArgs& a, int gran, int max_tiles, hipStream_t s);
+hipError_t launch_fc1_a8(const FcArgs& a, int max_tiles, hipStream_t s);
+hipError_t launch_fc2_a8(const FcArgs& a, int max_tiles, hipStream_t s);
 
 // Decode-shaped FC kernels (expert tiles of <= 16 activation rows); mode 0:
 // bf16 x group16, 1: bf16 x group32, 2: FP8 x group32, 3: MXFP4 x group32
@@ -106,6 +108,14 @@ hipError_t launch_fc_gemm_a8(const FcArgs& a, bool fc1, bool a4, bool prep, int 
 // N * K / 32 < 2^31.
 hipError_t launch_prepare_gemm(const uint8_t* src, const uint8_t* src_sf, uint8_t* dst, uint8_t* dst_sf,
                                int64_t E, int64_t N, int64_t K, bool w13, int w13_order, hipStream_t s);
+
+// Group16 weights (E2M1 + E4M3 [E, N, K/16] + global scale gs [E] or null)
+// -> the same GEMM layout with group32 UE8M0 scales, gs folded in
+// (moe_fp4_prepare_gemm_weights_g16): bit-identical to launch_requant_g16_g32
+// followed by launch_prepare_gemm.  N, K multiples of 512, N * K / 32 < 2^31.
+hipError_t launch_requant_prepare_gemm(const uint8_t* src, const uint8_t* src_sf, const float* gs, uint8_t* dst,
+                                       uint8_t* dst_sf, int64_t E, int64_t N, int64_t K, bool w13, int w13_order,
+                                       hipStream_t s);
 
 // out[t, :] = sum_j w[t, j] * y[slot_of[t*k + j], :]  (f32, or rounded to bf16)
 hipError_t launch_combine(const float* y, const int32_t* slot_of, const float* topk_w, int T,

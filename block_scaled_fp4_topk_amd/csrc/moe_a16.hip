@@ -252,17 +252,12 @@ hipError_t launch_one(const FcArgs& a, int max_tiles, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_fc1_a16(const FcArgs& a, int gran, int nt, int max_tiles, hipStream_t s) {
-  if (gran == 16) return nt == 1 ? launch_one<16, 1, true>(a, max_tiles, s)
-                                 : launch_one<16, 4, true>(a, max_tiles, s);
-  return nt == 1 ? launch_one<32, 1, true>(a, max_tiles, s) : launch_one<32, 4, true>(a, max_tiles, s);
+hipError_t launch_fc1_a16(const FcArgs& a, int gran, int max_tiles, hipStream_t s) {
+  return gran == 16 ? launch_one<16, 4, true>(a, max_tiles, s) : launch_one<32, 4, true>(a, max_tiles, s);
 }
 
-hipError_t launch_fc2_a16(const FcArgs& a, int gran, int nt, int max_tiles, hipStream_t s) {
-  if (gran == 16) return nt == 1 ? launch_one<16, 1, false>(a, max_tiles, s)
-                                 : launch_one<16, 4, false>(a, max_tiles, s);
-  return nt == 1 ? launch_one<32, 1, false>(a, max_tiles, s)
-                 : launch_one<32, 4, false>(a, max_tiles, s);
+hipError_t launch_fc2_a16(const FcArgs& a, int gran, int max_tiles, hipStream_t s) {
+  return gran == 16 ? launch_one<16, 4, false>(a, max_tiles, s) : launch_one<32, 4, false>(a, max_tiles, s);
 }
 
 }  // namespace moefp4

@@ -238,12 +238,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 }  // namespace
 
-hipError_t launch_fc1_a8(const FcArgs& a, int nt, int max_tiles, hipStream_t s) {
-  return nt == 1 ? launch_one<1, true>(a, max_tiles, s) : launch_one<4, true>(a, max_tiles, s);
+hipError_t launch_fc1_a8(const FcArgs& a, int max_tiles, hipStream_t s) {
+  return launch_one<4, true>(a, max_tiles, s);
 }
 
-hipError_t launch_fc2_a8(const FcArgs& a, int nt, int max_tiles, hipStream_t s) {
-  return nt == 1 ? launch_one<1, false>(a, max_tiles, s) : launch_one<4, false>(a, max_tiles, s);
+hipError_t launch_fc2_a8(const FcArgs& a, int max_tiles, hipStream_t s) {
+  return launch_one<4, false>(a, max_tiles, s);
 }
 
 hipError_t launch_combine(const float* y, const int32_t* slot_of, const float* topk_w, int T,

@@ -394,14 +394,15 @@ __global__ __launch_bounds__(256, 1) void fc_gemm_a8_kernel(FcArgs a, int nblk) 
   const int la1 = 16 * (8 * r16 + ((q + 4) ^ xr));            // token r16, piece q + 4
 
   // Stage in buffer b; g holds the stage's scale bytes in the low byte of
-  // each word; token groups at or past nv (the tile's valid rows) are not
-  // multiplied.  Reads: token groups 0 and 1, then the weight fragments in
-  // order, so that the first MFMAs wait only for the fragments they use;
-  // then each pair of token groups' MFMAs runs while the next pair's
-  // activation fragments are read.  hook(j), j = 0..15, runs after every 4
-  // MFMA slots (it issues the loads of a later stage).
+  // each word.  Every token group is multiplied, also the rows past the
+  // tile's valid ones (their results are never stored).  Reads: token
+  // groups 0 and 1, then the weight fragments in order, so that the first
+  // MFMAs wait only for the fragments they use; then each pair of token
+  // groups' MFMAs runs while the next pair's activation fragments are read.
+  // hook(j), j = 0..15, runs after every 4 MFMAs (it issues the loads of a
+  // later stage).
   constexpr int NX = A4 ? 1 : 2;  // LDS reads per activation fragment
-  auto compute = [&](uint32_t b, const LaneScales& g, int nv, auto&& hook, auto&& before_last)
+  auto compute = [&](uint32_t b, const LaneScales& g, auto&& hook, auto&& before_last)
       __attribute__((always_inline)) {
     const uint32_t sb = lds_addr(&ring.d[0]) + b * kStage;
     const uint32_t bw = sb + kW + 64 * wrow0 + lw;       // weight row group 0's fragment
@@ -445,19 +446,14 @@ __global__ __launch_bounds__(256, 1) void fc_gemm_a8_kernel(FcArgs a, int nblk) 
       hook(j);
       __builtin_amdgcn_sched_barrier(0);
     };
-    // token group tg's 8 MFMAs (if it holds a valid row), hooks 2 tg and 2 tg + 1
+    // token group tg's 8 MFMAs, hooks 2 tg and 2 tg + 1
     auto group = [&](auto tgi, auto&& before) __attribute__((always_inline)) {
       constexpr int tg = decltype(tgi)::value;
-      if (true) {
 #pragma unroll
-        for (int rg = 0; rg < 8; ++rg) {
-          before(rg);
-          mfma(tg, rg);
-          if (rg == 3 || rg == 7) hook_at(2 * tg + (rg >> 2));
-        }
-      } else {
-        hook_at(2 * tg);
-        hook_at(2 * tg + 1);
+      for (int rg = 0; rg < 8; ++rg) {
+        before(rg);
+        mfma(tg, rg);
+        if (rg == 3 || rg == 7) hook_at(2 * tg + (rg >> 2));
       }
     };
     auto none = [&](int) __attribute__((always_inline)) {};
@@ -671,7 +667,7 @@ __global__ __launch_bounds__(256, 1) void fc_gemm_a8_kernel(FcArgs a, int nblk) 
     // stage) are read under the last MFMAs
     const bool next_scales = P == GS - 1 && (!last_group || has_next);
     ScaleLines sl;
-    compute(bcur, gcur, cur.ne - cur.m0, [&](int j) __attribute__((always_inline)) {
+    compute(bcur, gcur, [&](int j) __attribute__((always_inline)) {
       if (j < kOps) issue_one(bnext, k2, j);
     }, [&]() __attribute__((always_inline)) {
       if (next_scales) issue_scale_reads(sl);

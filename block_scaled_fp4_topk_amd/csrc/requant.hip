@@ -77,7 +77,80 @@ __global__ __launch_bounds__(kThreads) void requant_kernel(const uint8_t* src, c
   }
 }
 
+// Group16 weights straight into the GEMM layout of the prefill kernels, with
+// group32 UE8M0 scales (the weight preparation of the DeepGEMM commit that
+// lets prepare_fp4_weights_for_mega_moe take raw grouped FP4 weights and
+// requantise them on the way into the fused kernel's layout).  Thread = one
+// row of a 512-row block over one 512-element scale group: 16 blocks of 32
+// (256 code bytes + 32 E4M3 bytes in), requantised as requant_kernel does;
+// each block's 16 code bytes are one 16-byte piece of the layout and the 16
+// new scale bytes one 16-byte scale piece.  Layout (moe_fp4_prepare_gemm_-
+// weights): code piece p of K stage s (128 elements) of block row i goes to
+// slot j = 4 i + (p ^ ((i >> 2) & 3)) of image (nb * K/128 + s); the scale
+// piece of (nb, g, i) is piece (nb * K/512 + g) * 512 + i.
+__global__ __launch_bounds__(kThreads) void requant_prepare_kernel(const uint8_t* __restrict__ src,
+                                                                   const uint8_t* __restrict__ src_sf,
+                                                                   const float* __restrict__ gs,
+                                                                   uint8_t* __restrict__ dst,
+                                                                   uint8_t* __restrict__ dst_sf, int N, int K,
+                                                                   int w13, int w13_order, int npieces) {
+  __shared__ float2 s_tab[256];
+  const int e = blockIdx.y;
+  const float g = gs ? gs[e] : 1.0f;
+  const uint32_t gneg = rq::bits(g) >> 31;
+  {
+    float p1, p3;
+    rq::ro_pair(threadIdx.x, fabsf(g), p1, p3);
+    s_tab[threadIdx.x] = float2{p1, p3};
+  }
+  __syncthreads();
+  const int cs = blockIdx.x * kThreads + threadIdx.x;
+  if (cs >= npieces) return;
+  const int ng = K >> 9;
+  const int i = cs & 511, bg = cs >> 9;  // block row, (row block, group)
+  const int nb = bg / ng, grp = bg - nb * ng;
+  int r = nb * 512 + i;  // source row
+  if (w13) {
+    const int i0 = nb * 256 + (i & 255);
+    r = ((i >= 256) != (w13_order != 0)) ? N / 2 + i0 : i0;
+  }
+  const size_t ecode = (size_t)e * N * (size_t)(K >> 1);
+  const uint8_t* sc = src + ecode + (size_t)r * (K >> 1) + 256 * grp;
+  const uint8_t* ss = src_sf + (size_t)e * N * (size_t)(K >> 4) + (size_t)r * (K >> 4) + 32 * grp;
+  const uint4 sa = *reinterpret_cast<const uint4*>(ss), sb = *reinterpret_cast<const uint4*>(ss + 16);
+  const uint32_t sw[8] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
+  const int sw_i = (i >> 2) & 3;
+  uint32_t ob[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int blk = 0; blk < 16; ++blk) {
+    const uint4 c = *reinterpret_cast<const uint4*>(sc + 16 * blk);
+    const uint32_t sf16 = (sw[blk >> 1] >> (16 * (blk & 1))) & 0xFFFFu;
+    const float2 ta = s_tab[sf16 & 0xFF], tb = s_tab[sf16 >> 8];
+    const uint32_t in[4] = {c.x, c.y, c.z, c.w};
+    uint32_t out[4];
+    const uint32_t b = rq::requant_block_tab(in, sf16, ta.x, ta.y, tb.x, tb.y, gneg, out);
+    ob[blk >> 2] |= b << (8 * (blk & 3));
+    const int st = 4 * grp + (blk >> 2), piece = blk & 3;
+    const int j = 4 * i + (piece ^ sw_i);
+    *reinterpret_cast<uint4*>(dst + ecode + ((size_t)(nb * (K >> 7) + st) * 2048 + j) * 16) =
+        uint4{out[0], out[1], out[2], out[3]};
+  }
+  *reinterpret_cast<uint4*>(dst_sf + (size_t)e * N * (size_t)(K >> 5) + (size_t)cs * 16) =
+      uint4{ob[0], ob[1], ob[2], ob[3]};
+}
+
 }  // namespace
+
+hipError_t launch_requant_prepare_gemm(const uint8_t* src, const uint8_t* src_sf, const float* gs, uint8_t* dst,
+                                       uint8_t* dst_sf, int64_t E, int64_t N, int64_t K, bool w13, int w13_order,
+                                       hipStream_t s) {
+  const int64_t npieces = N * K / 512;  // scale pieces per expert
+  if (E <= 0 || npieces <= 0) return hipSuccess;
+  const int64_t gx = (npieces + kThreads - 1) / kThreads;
+  hipLaunchKernelGGL(requant_prepare_kernel, dim3((unsigned)gx, (unsigned)E), dim3(kThreads), 0, s, src, src_sf, gs,
+                     dst, dst_sf, (int)N, (int)K, w13 ? 1 : 0, w13_order, (int)npieces);
+  return hipGetLastError();
+}
 
 hipError_t launch_requant_g16_g32(const uint8_t* src, const uint8_t* src_sf, const float* gs,
                                   uint8_t* dst, uint8_t* dst_sf, int64_t E, int64_t N, int64_t K,

@@ -116,6 +116,20 @@ typedef struct moefp4_problem {
  * whose expert id was outside [0, E) and was therefore dropped. */
 moefp4_status moe_fp4_workspace_bytes(const moefp4_problem* p, size_t* bytes);
 
+/* Where a forward on problem p keeps, in its workspace, the intermediate h
+ * that FC2 consumes (byte offsets from the workspace start): *h: h [A, I] in
+ * expert-slot order, A = T * top_k -- bfloat16 for BF16 activations, E4M3
+ * bytes for FP8 activations, two E2M1 codes per byte ([A, I/2], element 2j in
+ * the low nibble of byte j) for FP4 activations; *h_sf: its UE8M0 scales
+ * [A, I/32] (FP8 / FP4 activations; 0 otherwise); *slot_of: the int32 [A]
+ * map from assignment t * top_k + j to its slot (-1: dropped).  After a
+ * forward completes these regions hold the values of that call (the h
+ * quantisation of SwiGLU's output: bf16 RNE, or E4M3 / E2M1 + UE8M0 per 32).
+ * For tests and debugging of the quantisation decisions; EINVAL / EUNSUPPORTED
+ * as moe_fp4_workspace_bytes. */
+moefp4_status moe_fp4_workspace_offsets(const moefp4_problem* p, size_t* h, size_t* h_sf,
+                                        size_t* slot_of);
+
 /* Routing: groups the T*k assignments a = t*k + j by expert id, stably (ties
  * in a-order).  Device outputs: counts [E], offsets [E+1] (exclusive prefix,
  * offsets[E] = number of valid assignments), sorted_assign [T*k] (assignment
@@ -176,6 +190,26 @@ moefp4_status moe_fp4_prepare_gemm_weights(int64_t E, int64_t N, int64_t K, int3
                                            int32_t w13_order, const uint8_t* src,
                                            const uint8_t* src_sf, uint8_t* dst, uint8_t* dst_sf,
                                            hipStream_t stream);
+
+/* Group16 NVFP4 weights straight into the GEMM layout, in one pass: the
+ * requantisation of fp4_requant_gran_k (dequantise with the group16 E4M3
+ * scales and the per-expert global scale, UE8M0 e = ceil(log2(amax / 6)) per
+ * block of 32, E2M1 RNE codes; the global scale folded in) written in the
+ * layout of moe_fp4_prepare_gemm_weights.  The counterpart of the weight
+ * preparation of [P1] that accepts raw grouped FP4 weights and scales and
+ * performs the optional requantisation and the layout transform in one call
+ * (prepare_fp4_weights_for_mega_moe).  Output bit-identical to
+ * fp4_requant_gran_k followed by moe_fp4_prepare_gemm_weights.
+ * src [E, N, K/2] uint8, src_sf [E, N, K/16] E4M3 bytes, src_gs [E] float32 or
+ * NULL (1), dst [E, N, K/2] uint8, dst_sf [E, N, K/32] uint8 (UE8M0, GEMM
+ * layout); which / w13_order as for moe_fp4_prepare_gemm_weights.  Device
+ * memory, 16-byte aligned, pairwise disjoint (EINVAL otherwise); N and K
+ * multiples of 512 (EINVAL otherwise).  The forward then takes dst / dst_sf
+ * with gran_k = 32, w_layout = GEMM and no global scale. */
+moefp4_status moe_fp4_prepare_gemm_weights_g16(int64_t E, int64_t N, int64_t K, int32_t which,
+                                               int32_t w13_order, const uint8_t* src,
+                                               const uint8_t* src_sf, const float* src_gs,
+                                               uint8_t* dst, uint8_t* dst_sf, hipStream_t stream);
 
 /* Requantise E x [N, K] FP4 from src_gran to dst_gran ([P2] Requantization
  * path; [P1] requant_fp4_to_gran_k): dequantise with the group16 E4M3 scales

@@ -33,6 +33,7 @@ from .formats import (  # noqa: F401
     rne_e4m3,
     rne_bf16,
     dequant_fp4,
+    bf16_bits_decode,
 )
 from .requant import requant_g16_to_g32, requant_block  # noqa: F401
-from .moe import route, moe_forward, quantize_h_a8, quantize_a4, silu, h_decision_band  # noqa: F401
+from .moe import route, moe_forward, quantize_h_a8, quantize_a4, silu, h_decision_band, h_decision_margin, decision_radius  # noqa: F401

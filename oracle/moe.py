@@ -122,11 +122,44 @@ E2M1_POS = e2m1_decode(np.arange(8, dtype=np.uint8))  # magnitudes of codes 0..7
 
 
 # A rounding decision of h is taken as undecided between its two
-# neighbouring results when h lies within DECISION_RADIUS * (max |h| of its
-# 32-element block) of the decision boundary.  An FP32-accumulated h (the
-# kernels') stays within about 2**-20 of that block maximum of the exact one,
-# cancellation included, so this leaves a wide margin.
-DECISION_RADIUS = 2.0 ** -14
+# neighbouring results when h lies within a decision radius times the maximum
+# |h| of its 32-element block of the decision boundary.  The radius bounds how
+# far the GPU's computation of h can land from the exact one.
+#
+# DECISION_RADIUS (bfloat16 activations on the bf16 / fp16 matrix
+# instructions, and FP4 activations on the FP4 x FP4 block-scaled one):
+#  * FC1 products are exact in FP32 (an E2M1 code times an E4M3 or power-of-
+#    two block scale has at most 6 significant bits, a bfloat16 / fp16 / E2M1
+#    activation at most 11), the global scale is one multiplication after the
+#    sum, so the only FP32 error of G is its accumulation: at most K - 1
+#    roundings of relative size <= 2**-24, fewest errors to the sequential
+#    order's most;
+#  * under the usual model of independent rounding errors the accumulated
+#    error is about 2**-24 * sqrt(sum of squared partial sums) (Higham and
+#    Mary, probabilistic rounding error analysis, 2019); for the workloads'
+#    shapes the sequential FP32 order of K = 6144 exact products, followed by
+#    SwiGLU in FP32, lands within 2**-19 of the block maximum of the exact h
+#    (the CPU pin test_decision_radius_covers_fp32 checks this on decode,
+#    prefill and tiny shapes);
+#  * SwiGLU in FP32 with a hardware exp and reciprocal adds a few ulp of |h|
+#    <= the block maximum, below 2**-21 of it.
+# 2**-17 is four times the larger of those.
+DECISION_RADIUS = 2.0 ** -17
+# DECISION_RADIUS_FP8 (FP8 activations on the FP8 x FP4 block-scaled matrix
+# instruction of the GPU): that instruction does not add its 128 products
+# exactly -- measured on MI355X, one instruction's result is off by up to
+# 2**-12.8 of its largest product on Gaussian FP8 data and 2**-10.9 on data
+# spanning 16 binades, while FP4 x FP4 and bf16 products sum exactly there --
+# so G carries errors far above FP32 rounding.  Over every FP8 parity case the
+# GPU's quantised h differs from the exact one's only where h lies within
+# 2**-14.8 of a block maximum of a boundary; 2**-13 is 3.5 times that.
+DECISION_RADIUS_FP8 = 2.0 ** -13
+
+
+def decision_radius(a8, a4=False):
+    """The decision radius of the path: FP8 activations (a8 and not a4), or
+    the FP32-accurate paths."""
+    return DECISION_RADIUS_FP8 if a8 and not a4 else DECISION_RADIUS
 
 
 def _grid_ambiguity(y, mant_bits, emin, radius):
@@ -143,13 +176,16 @@ def _grid_ambiguity(y, mant_bits, emin, radius):
     return np.where(near, quantum, 0.0)
 
 
-def h_decision_band(h, a8, radius=DECISION_RADIUS, a4=False):
+def h_decision_band(h, a8, radius=None, a4=False):
     """Per element, the largest change of the quantised h that a rounding
-    decision within ``radius`` * (block max |h|) could make: one grid step
+    decision within ``radius`` (default: the path's decision_radius) * (block
+    max |h|) could make: one grid step
     where h is that close to a rounding midpoint and, for A8 / A4, the whole
     requantisation of a 32-block under the neighbouring exponent where amax
     is that close to 448 * 2**e (6 * 2**e).  Zero where every decision is
     clear."""
+    if radius is None:
+        radius = decision_radius(a8, a4)
     h = np.asarray(h, dtype=np.float64)
     n, I = h.shape
     blk = h.reshape(n, I // 32, 32)
@@ -185,6 +221,41 @@ def h_decision_band(h, a8, radius=DECISION_RADIUS, a4=False):
     return band.reshape(n, I)
 
 
+def h_decision_margin(h, a8, a4=False):
+    """Per element, the distance from the exact h to the nearest boundary at
+    which its quantisation decision changes, divided by the maximum |h| of
+    its 32-element block: the rounding midpoint of its grid (bf16; or E4M3 /
+    E2M1 after the block's UE8M0 scaling) and, for A8 / A4, the block's
+    exponent boundaries 448 * 2**(e-1), 448 * 2**e (6 * 2**(e-1), 6 * 2**e)
+    around max |h|.  An FP32 h closer than this to the exact one is
+    quantised as the exact one is.  All-zero blocks get +inf."""
+    h = np.asarray(h, dtype=np.float64)
+    n, I = h.shape
+    blk = np.abs(h.reshape(n, I // 32, 32))
+    amax = np.max(blk, axis=-1)
+
+    def grid_dist(y, mant_bits, emin):
+        _, ex = np.frexp(y)
+        e = np.maximum(ex.astype(np.int64) - 1, emin)
+        quantum = np.ldexp(1.0, e - mant_bits)
+        frac = y / quantum - np.floor(y / quantum)
+        return np.abs(frac - 0.5) * quantum
+
+    if not a8 and not a4:
+        dist = grid_dist(blk, 7, -126)
+    else:
+        top, mant, emin = (6.0, 1, 0) if a4 else (448.0, 3, -6)
+        _, _, sb = quantize_a4(h) if a4 else quantize_h_a8(h)
+        e = sb.astype(np.int64) - 127
+        dist = np.ldexp(grid_dist(np.ldexp(blk, -e[..., None]), mant, emin), e[..., None])
+        lo, hi = np.ldexp(top, e - 1), np.ldexp(top, e)
+        dexp = np.minimum(np.abs(amax - lo), np.abs(hi - amax))
+        dist = np.minimum(dist, dexp[..., None])
+    with np.errstate(divide="ignore", invalid="ignore"):
+        m = np.where(amax[..., None] > 0, dist / amax[..., None], np.inf)
+    return m.reshape(n, I)
+
+
 def decode_activations(x, x_sf=None, a4=False):
     """A16: x is [T, H] bfloat16 bit patterns (uint16).  A8: x is [T, H]
     E4M3 bytes and x_sf [T, H/32] UE8M0 bytes; value = fp8 * 2**(sf - 127).
@@ -198,7 +269,8 @@ def decode_activations(x, x_sf=None, a4=False):
 
 def moe_forward(x, topk_ids, topk_w, w13, w13_sf, w13_gs, w2, w2_sf, w2_gs,
                 gran: int, x_sf=None, w13_order: str = "gate_up",
-                tokens=None, out_cols=None, return_parts=False, return_band=False, a4=False):
+                tokens=None, out_cols=None, return_parts=False, return_band=False, a4=False,
+                return_h=False):
     """FP64 MoE forward.  Shapes: x [T, H] (see decode_activations),
     topk_ids/topk_w [T, k], w13 [E, 2I, H/2], w13_sf [E, 2I, H/gran],
     w2 [E, H, I/2], w2_sf [E, H, I/gran], gs [E] float32 or None.
@@ -211,6 +283,9 @@ def moe_forward(x, topk_ids, topk_w, w13, w13_sf, w13_gs, w2, w2_sf, w2_gs,
     ``tokens`` / ``out_cols`` restrict the computation to a subset of output
     rows / columns (each output element is computed by the same definition);
     the result is then [len(tokens), len(out_cols)].
+
+    ``return_h``: also return {slot: (h, hhat)}, the exact SwiGLU output and
+    its quantised value (the FC2 input) per computed assignment.
 
     ``return_band``: also return, per output element, the largest change
     that near-tie rounding decisions of h (see h_decision_band) can cause:
@@ -229,6 +304,7 @@ def moe_forward(x, topk_ids, topk_w, w13, w13_sf, w13_gs, w2, w2_sf, w2_gs,
     a8 = x_sf is not None and not a4
     tokens = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
     out_cols = np.arange(H) if out_cols is None else np.asarray(out_cols, dtype=np.int64)
+    hrows = {}  # slot -> (exact h row, quantised h row), for return_h
 
     counts, offsets, sorted_assign, slot_of = route(ids, E)
     xv = decode_activations(x, x_sf, a4)
@@ -257,6 +333,9 @@ def moe_forward(x, topk_ids, topk_w, w13, w13_sf, w13_gs, w2, w2_sf, w2_gs,
             raise ValueError(w13_order)
         h = silu(gate) * up
         hhat = quantize_a4(h)[0] if a4 else quantize_h_a8(h)[0] if a8 else rne_bf16(h)
+        if return_h:
+            for r, a in enumerate(assigns):
+                hrows[int(slot_of[a])] = (h[r], hhat[r])
         W2 = dequant_fp4(np.asarray(w2[e])[out_cols], np.asarray(w2_sf[e])[out_cols],
                          gran, kind, gs2)
         Ye = hhat @ W2.T
@@ -281,4 +360,6 @@ def moe_forward(x, topk_ids, topk_w, w13, w13_sf, w13_gs, w2, w2_sf, w2_gs,
         res += ((counts, offsets, sorted_assign, slot_of),)
     if return_band:
         res += (band,)
+    if return_h:
+        res += (hrows,)
     return res[0] if len(res) == 1 else res

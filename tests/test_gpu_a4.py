@@ -15,7 +15,7 @@ import block_scaled_fp4_topk_amd as moe
 import oracle
 from oracle.moe import decode_activations
 import synth
-from helpers import check_bound, gpu_forward, require_gpu, to_dev
+from helpers import check_bound, check_h, forward_ws, gpu_forward, require_gpu, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -77,7 +77,7 @@ def test_quantize_act_fp4_bit_exact(name, gen, T, H):
 def _a4_ref(inp, x4, x4sf, tokens=None, out_cols=None):
     return oracle.moe_forward(x4, inp.topk_ids, inp.topk_w, inp.w13, inp.w13_sf, inp.w13_gs,
                               inp.w2, inp.w2_sf, inp.w2_gs, inp.cfg.gran, x_sf=x4sf, a4=True,
-                              tokens=tokens, out_cols=out_cols, return_band=True)
+                              tokens=tokens, out_cols=out_cols, return_band=True, return_h=True)
 
 
 FWD = [
@@ -101,7 +101,7 @@ def test_forward_a4(cfg):
     inp = synth.make_moe_inputs(cfg)
     d = to_dev(inp)
     # the library quantises bf16 x ...
-    f32 = gpu_forward(inp, d, out_dtype=torch.float32, quantize_x="fp4")
+    f32, ws, p = forward_ws(inp, d, quantize_x="fp4")
     b16 = gpu_forward(inp, d, quantize_x="fp4")
     # ... or takes caller-quantised MXFP4 x: the same bits
     _, x4, x4sf = oracle.quantize_a4(decode_activations(inp.x))
@@ -110,7 +110,8 @@ def test_forward_a4(cfg):
     torch.cuda.synchronize()
     assert torch.equal(f32.to(torch.bfloat16).view(torch.int16), b16.view(torch.int16))
     assert torch.equal(f32.view(torch.int32), f32b.view(torch.int32))
-    ref, band = _a4_ref(inp, x4, x4sf)
+    ref, band, hrows = _a4_ref(inp, x4, x4sf)
+    check_h(ws, p, hrows, "A4 forward")
     check_bound(f32.cpu().numpy().astype(np.float64), ref, "A4 forward", band)
 
 
@@ -123,14 +124,15 @@ def test_full_decode_a4_sampled():
     inp = synth.make_moe_inputs(cfg)
     d = to_dev(inp)
     print("decode32 A4: running on GPU", flush=True)
-    out = gpu_forward(inp, d, out_dtype=torch.float32, quantize_x="fp4")
+    out, ws, p = forward_ws(inp, d, quantize_x="fp4")
     torch.cuda.synchronize()
     rng = np.random.default_rng(2)
     tokens = sorted({0, cfg.T - 1, int(rng.integers(cfg.T)), int(rng.integers(cfg.T))})
     cols = np.sort(rng.choice(cfg.H, size=768, replace=False))
     _, x4, x4sf = oracle.quantize_a4(decode_activations(inp.x))
     print(f"decode32 A4: oracle on tokens {tokens}", flush=True)
-    ref, band = _a4_ref(inp, x4, x4sf, tokens=tokens, out_cols=cols)
+    ref, band, hrows = _a4_ref(inp, x4, x4sf, tokens=tokens, out_cols=cols)
+    check_h(ws, p, hrows, "decode32 A4 sampled")
     got = out[tokens][:, torch.from_numpy(cols).cuda()].cpu().numpy().astype(np.float64)
     check_bound(got, ref, "decode32 A4 sampled", band)
 
@@ -145,7 +147,7 @@ def test_full_prefill_a4_sampled():
     inp = synth.make_moe_inputs(cfg)
     d = to_dev(inp)
     print("prefill32 A4: running on GPU", flush=True)
-    out = gpu_forward(inp, d, out_dtype=torch.float32, quantize_x="fp4")
+    out, ws, p = forward_ws(inp, d, quantize_x="fp4")
     torch.cuda.synchronize()
     rng = np.random.default_rng(1)
     counts = np.bincount(inp.topk_ids.ravel(), minlength=cfg.E)
@@ -154,6 +156,7 @@ def test_full_prefill_a4_sampled():
     cols = np.sort(rng.choice(cfg.H, size=768, replace=False))
     _, x4, x4sf = oracle.quantize_a4(decode_activations(inp.x))
     print(f"prefill32 A4: oracle on tokens {tokens}", flush=True)
-    ref, band = _a4_ref(inp, x4, x4sf, tokens=tokens, out_cols=cols)
+    ref, band, hrows = _a4_ref(inp, x4, x4sf, tokens=tokens, out_cols=cols)
+    check_h(ws, p, hrows, "prefill32 A4 sampled")
     got = out[tokens][:, torch.from_numpy(cols).cuda()].cpu().numpy().astype(np.float64)
     check_bound(got, ref, "prefill32 A4 sampled", band)

@@ -27,13 +27,13 @@ FMT_IDS = ["bf16-g16", "bf16-g32", "fp8-g32"]
 def _ref(inp):
     return oracle.moe_forward(inp.x, inp.topk_ids, inp.topk_w, inp.w13, inp.w13_sf, inp.w13_gs,
                               inp.w2, inp.w2_sf, inp.w2_gs, inp.cfg.gran, x_sf=inp.x_sf,
-                              return_band=True)
+                              return_band=True, return_h=True)
 
 
 def _check(inp, what):
     d = to_dev(inp)
-    ref, band = _ref(inp)
-    check_forward(inp, d, ref, what, band=band)
+    ref, band, hrows = _ref(inp)
+    check_forward(inp, d, ref, what, band=band, hrows=hrows)
 
 
 @pytest.mark.parametrize("fmt", FORMATS, ids=FMT_IDS)
@@ -125,8 +125,8 @@ def test_dropped_only_token():
     out = gpu_forward(inp, d, out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert torch.count_nonzero(out[2]).item() == 0
-    ref, band = _ref(inp)
-    check_forward(inp, d, ref, "dropped-only token", band=band)
+    ref, band, hrows = _ref(inp)
+    check_forward(inp, d, ref, "dropped-only token", band=band, hrows=hrows)
     ws = torch.empty(moe.workspace_bytes(moe.make_problem(cfg.T, cfg.E, cfg.k, cfg.H, cfg.I, cfg.gran)),
                      dtype=torch.uint8, device="cuda")
     gpu_forward(inp, d, workspace=ws)

@@ -9,18 +9,19 @@ import pytest
 import torch
 
 import oracle
+from oracle.moe import decode_activations
 import synth
-from helpers import check_bound, check_forward, gpu_forward, require_gpu, to_dev
+from helpers import check_bound, check_forward, check_h, forward_ws, gpu_forward, require_gpu, to_dev
 
 pytestmark = pytest.mark.gpu
 
 
-def ref_forward(inp, order="gate_up", tokens=None, out_cols=None):
-    """(FP64 output, decision band) of the oracle."""
+def ref_forward(inp, order="gate_up", tokens=None, out_cols=None, return_h=False):
+    """(FP64 output, decision band[, {slot: (h, hhat)}]) of the oracle."""
     return oracle.moe_forward(inp.x, inp.topk_ids, inp.topk_w, inp.w13, inp.w13_sf, inp.w13_gs,
                               inp.w2, inp.w2_sf, inp.w2_gs, inp.cfg.gran, x_sf=inp.x_sf,
                               w13_order=order, tokens=tokens, out_cols=out_cols,
-                              return_band=True)
+                              return_band=True, return_h=return_h)
 
 
 def combos(base):
@@ -63,8 +64,45 @@ def test_forward_small(cfg):
     inp = synth.make_moe_inputs(cfg)
     d = to_dev(inp)
     for order in ("gate_up", "up_gate"):
-        ref, band = ref_forward(inp, order)
-        check_forward(inp, d, ref, f"{_id(cfg)} {order}", order, band)
+        ref, band, hrows = ref_forward(inp, order, return_h=True)
+        check_forward(inp, d, ref, f"{_id(cfg)} {order}", order, band, hrows)
+
+
+# FP8 activations (caller-quantised, or bf16 x the library quantises) on the
+# 64-row tiles: more than 16 assignments per active expert with H or I not a
+# multiple of 512 (the prefill GEMM's row blocks), several tiles per expert,
+# ragged tails, several weight-row blocks
+MID_FP8 = [
+    synth.variant(synth.CONFIGS["tiny"], T=300, E=4, k=2, H=768, I=512, seed=27, gran=32, act="fp8",
+                  global_scale="none", routing="zipf"),
+    synth.variant(synth.CONFIGS["tiny"], T=300, E=4, k=2, H=1024, I=1280, seed=28, gran=32, act="fp8",
+                  global_scale="uniform"),
+    synth.variant(synth.CONFIGS["tiny"], T=300, E=4, k=2, H=768, I=1280, seed=29, gran=32, act="bf16q",
+                  global_scale="none", routing="zipf"),
+]
+
+
+@pytest.mark.parametrize("cfg", MID_FP8, ids=[_id(c) for c in MID_FP8])
+def test_forward_fp8_64row_tiles(cfg):
+    require_gpu()
+    print("forward 64-row FP8 tiles", _id(cfg), flush=True)
+    inp = synth.make_moe_inputs(cfg)
+    active = np.unique(inp.topk_ids).size
+    # the dispatch rule of the forward for this kernel
+    assert inp.topk_ids.size / active > 16 and (cfg.H % 512 or cfg.I % 512)
+    d = to_dev(inp)
+    quant = cfg.act == "bf16q"
+    if quant:
+        # the oracle runs on its own FP8 quantisation of x (the library's is
+        # bit-exact with it, test_gpu_quant)
+        _, codes, sf = oracle.quantize_h_a8(decode_activations(inp.x))
+        rinp = synth.MoEInputs(cfg, codes, sf, inp.topk_ids, inp.topk_w, inp.w13, inp.w13_sf, inp.w13_gs,
+                               inp.w2, inp.w2_sf, inp.w2_gs)
+    else:
+        rinp = inp
+    for order in ("gate_up", "up_gate"):
+        ref, band, hrows = ref_forward(rinp, order, return_h=True)
+        check_forward(inp, d, ref, f"{_id(cfg)} {order}", order, band, hrows, quantize_x=quant)
 
 
 def test_duplicate_and_dropped_ids():
@@ -78,8 +116,8 @@ def test_duplicate_and_dropped_ids():
     ids[3] = ids[3, 0]             # all three picks the same expert
     inp.topk_ids = ids
     d = to_dev(inp)
-    ref, band = ref_forward(inp)
-    check_forward(inp, d, ref, "dup+dropped", band=band)
+    ref, band, hrows = ref_forward(inp, return_h=True)
+    check_forward(inp, d, ref, "dup+dropped", band=band, hrows=hrows)
 
 
 def test_deterministic():
@@ -115,7 +153,7 @@ def test_full_size_sampled(name):
     require_gpu()
     inp, d = full_inputs(name)
     print(f"{name}: running on GPU", flush=True)
-    out = gpu_forward(inp, d, out_dtype=torch.float32)
+    out, ws, p = forward_ws(inp, d)
     b16 = gpu_forward(inp, d)
     torch.cuda.synchronize()
     assert torch.equal(out.to(torch.bfloat16).view(torch.int16), b16.view(torch.int16))
@@ -125,9 +163,40 @@ def test_full_size_sampled(name):
     tokens = sorted({0, inp.cfg.T - 1, heavy, int(rng.integers(inp.cfg.T))})
     cols = np.sort(rng.choice(inp.cfg.H, size=768, replace=False))
     print(f"{name}: oracle on tokens {tokens}", flush=True)
-    ref, band = ref_forward(inp, tokens=tokens, out_cols=cols)
+    ref, band, hrows = ref_forward(inp, tokens=tokens, out_cols=cols, return_h=True)
+    check_h(ws, p, hrows, f"{name} sampled")
     got = out[tokens][:, torch.from_numpy(cols).cuda()].cpu().numpy().astype(np.float64)
     check_bound(got, ref, f"{name} sampled", band)
+
+
+def test_full_prefill_ragged_tiles_sampled():
+    """prefill32 in the benchmark's launch configuration, sampled where the
+    128-row expert tiles are partly filled: for 16 experts spread over the
+    Zipf load range (lightest to heaviest), the token of the expert's last
+    assignment (in its last, ragged tile), plus the first and last tokens;
+    512 sampled output columns."""
+    require_gpu()
+    inp, d = full_inputs("prefill32")
+    cfg = inp.cfg
+    print("prefill32 ragged tiles: running on GPU", flush=True)
+    out, ws, p = forward_ws(inp, d)
+    torch.cuda.synchronize()
+    flat = inp.topk_ids.ravel()
+    counts = np.bincount(flat, minlength=cfg.E)
+    by_load = np.argsort(counts, kind="stable")
+    active = by_load[counts[by_load] > 0]
+    picked = active[np.linspace(0, active.size - 1, 16).round().astype(int)]
+    tokens = {0, cfg.T - 1}
+    for e in picked:
+        tokens.add(int(np.flatnonzero(flat == e)[-1] // cfg.k))
+    tokens = sorted(tokens)
+    print(f"prefill32 ragged tiles: experts {picked.tolist()} with {counts[picked].tolist()} assignments "
+          f"(last tile rows {(counts[picked] - 1) % 128 + 1}); oracle on tokens {tokens}", flush=True)
+    cols = np.sort(np.random.default_rng(5).choice(cfg.H, size=512, replace=False))
+    ref, band, hrows = ref_forward(inp, tokens=tokens, out_cols=cols, return_h=True)
+    check_h(ws, p, hrows, "prefill32 ragged tiles sampled")
+    got = out[tokens][:, torch.from_numpy(cols).cuda()].cpu().numpy().astype(np.float64)
+    check_bound(got, ref, "prefill32 ragged tiles sampled", band)
 
 
 def test_many_items_per_workgroup():
@@ -140,12 +209,13 @@ def test_many_items_per_workgroup():
     inp = synth.make_moe_inputs(cfg)
     d = to_dev(inp)
     print(f"many items: T={cfg.T} E={cfg.E} H={cfg.H} I={cfg.I}: running on GPU", flush=True)
-    out = gpu_forward(inp, d, out_dtype=torch.float32)
+    out, ws, p = forward_ws(inp, d)
     torch.cuda.synchronize()
     rng = np.random.default_rng(1)
     tokens = sorted({0, cfg.T - 1, int(rng.integers(cfg.T)), int(rng.integers(cfg.T))})
     cols = np.sort(rng.choice(cfg.H, size=768, replace=False))
     print(f"many items: oracle on tokens {tokens}", flush=True)
-    ref, band = ref_forward(inp, tokens=tokens, out_cols=cols)
+    ref, band, hrows = ref_forward(inp, tokens=tokens, out_cols=cols, return_h=True)
+    check_h(ws, p, hrows, "many items sampled")
     got = out[tokens][:, torch.from_numpy(cols).cuda()].cpu().numpy().astype(np.float64)
     check_bound(got, ref, "many items sampled", band)

@@ -2,16 +2,19 @@
 the layout's definition (written out here in numpy from the header's
 formulas), and a forward on prepared weights equals the forward on the RAW
 weights bit for bit (same kernel arithmetic, only the weight addressing
-differs), at prefill shapes with FP8 and FP4 activations, both w13 orders,
-and at the full prefill workload."""
+differs) and meets the accuracy bound against the oracle, at prefill shapes
+with FP8 and FP4 activations, both w13 orders, and at the full prefill
+workload."""
 
 import numpy as np
 import pytest
 import torch
 
 import block_scaled_fp4_topk_amd as moe
+import oracle
+from oracle.moe import decode_activations
 import synth
-from helpers import gpu_forward, require_gpu, to_dev
+from helpers import check_bound, check_h, forward_ws, gpu_forward, require_gpu, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -88,9 +91,19 @@ def test_forward_prepared_equals_raw(cfg, order):
     q = {"bf16q4": "fp4"}.get(cfg.act, False)
     raw = gpu_forward(inp, d, order, out_dtype=torch.float32, quantize_x=q)
     pd = prepared(d, order)
-    prep = gpu_forward(inp, pd, order, out_dtype=torch.float32, quantize_x=q, w_layout="gemm")
+    prep, ws, p = forward_ws(inp, pd, order, quantize_x=q, w_layout="gemm")
     torch.cuda.synchronize()
     assert torch.equal(raw.view(torch.int32), prep.view(torch.int32))
+    # and the forward on prepared weights against the oracle directly
+    if cfg.act == "bf16q4":
+        _, xr, xr_sf = oracle.quantize_a4(decode_activations(inp.x))
+    else:
+        xr, xr_sf = inp.x, inp.x_sf
+    ref, band, hrows = oracle.moe_forward(xr, inp.topk_ids, inp.topk_w, inp.w13, inp.w13_sf, inp.w13_gs, inp.w2,
+                                          inp.w2_sf, inp.w2_gs, cfg.gran, x_sf=xr_sf, w13_order=order,
+                                          a4=cfg.act == "bf16q4", return_band=True, return_h=True)
+    check_h(ws, p, hrows, f"GEMM-layout forward {cfg.act} {order}")
+    check_bound(prep.cpu().numpy().astype(np.float64), ref, f"GEMM-layout forward {cfg.act} {order}", band)
 
 
 def test_full_prefill_prepared_equals_raw():
@@ -104,3 +117,55 @@ def test_full_prefill_prepared_equals_raw():
     prep = gpu_forward(inp, prepared(d), out_dtype=torch.float32, w_layout="gemm")
     torch.cuda.synchronize()
     assert torch.equal(raw.view(torch.int32), prep.view(torch.int32))
+
+
+@pytest.mark.parametrize("which,N,K,order", [("w13", 1024, 1024, 0), ("w13", 1024, 1536, 1), ("w2", 1536, 1024, 0)])
+def test_prepare_g16_matches_requant_then_prepare(which, N, K, order):
+    """The one-pass group16 -> GEMM-layout group32 preparation equals the
+    requantisation followed by the reorder, bit for bit, and the oracle's
+    requantisation laid out by the layout's definition."""
+    require_gpu()
+    print(f"prepare g16 {which} N={N} K={K} order={order}", flush=True)
+    E = 3
+    src = np.empty((E, N, K // 2), np.uint8)
+    sf = np.empty((E, N, K // 16), np.uint8)
+    for e in range(E):
+        src[e], sf[e] = synth.make_fp4_tensor(91, 10, e, N, K, 16, (-10.0, -3.0))
+    gs = np.array([0.75, -1.5, 1.25], np.float32)  # a negative global scale flips signs
+    ts, tsf, tgs = (torch.from_numpy(a).cuda() for a in (src, sf, gs))
+    d, dsf = moe.prepare_gemm_weights_g16(ts, tsf, tgs, which, order)
+    r, rsf = moe.requant_gran_k(ts, tsf, tgs)
+    p, psf = moe.prepare_gemm_weights(r, rsf, which, order)
+    torch.cuda.synchronize()
+    assert torch.equal(d, p) and torch.equal(dsf, psf)
+    rd, rdsf = oracle.requant_g16_to_g32(src, sf, gs)
+    ld, ldsf = gemm_layout_ref(rd, rdsf, which == "w13", order)
+    assert np.array_equal(d.cpu().numpy(), ld)
+    assert np.array_equal(dsf.cpu().numpy(), ldsf)
+
+
+@pytest.mark.parametrize("order", ["gate_up", "up_gate"])
+def test_forward_on_g16_prepared_weights(order):
+    """A group16 NVFP4 layer prepared in one pass (requantised to group32
+    with the global scales folded in, GEMM layout) runs the FP8 x FP4
+    prefill GEMM; the oracle runs the same layer requantised by its own
+    arithmetic."""
+    require_gpu()
+    cfg = synth.variant(synth.CONFIGS["tiny"], T=400, E=4, k=2, H=1536, I=1024, seed=92, gran=16, act="fp8",
+                        global_scale="uniform", routing="zipf")
+    print(f"forward on g16-prepared weights order={order}", flush=True)
+    inp = synth.make_moe_inputs(cfg)
+    d = to_dev(inp)
+    pd = dict(d, w13_gs=None, w2_gs=None)
+    pd["w13"], pd["w13_sf"] = moe.prepare_gemm_weights_g16(d["w13"], d["w13_sf"], d["w13_gs"], "w13", order)
+    pd["w2"], pd["w2_sf"] = moe.prepare_gemm_weights_g16(d["w2"], d["w2_sf"], d["w2_gs"], "w2")
+    g32 = synth.variant(cfg, gran=32, global_scale="none")
+    out, ws, p = forward_ws(synth.MoEInputs(g32, inp.x, inp.x_sf, inp.topk_ids, inp.topk_w, None, None, None,
+                                            None, None, None), pd, order, w_layout="gemm")
+    torch.cuda.synchronize()
+    w13, w13_sf = oracle.requant_g16_to_g32(inp.w13, inp.w13_sf, inp.w13_gs)
+    w2, w2_sf = oracle.requant_g16_to_g32(inp.w2, inp.w2_sf, inp.w2_gs)
+    ref, band, hrows = oracle.moe_forward(inp.x, inp.topk_ids, inp.topk_w, w13, w13_sf, None, w2, w2_sf, None, 32,
+                                          x_sf=inp.x_sf, w13_order=order, return_band=True, return_h=True)
+    check_h(ws, p, hrows, f"g16-prepared forward {order}")
+    check_bound(out.cpu().numpy().astype(np.float64), ref, f"g16-prepared forward {order}", band)

@@ -13,7 +13,7 @@ import block_scaled_fp4_topk_amd as moe
 import oracle
 from oracle.moe import decode_activations
 import synth
-from helpers import check_bound, gpu_forward, require_gpu, to_dev
+from helpers import check_bound, check_h, forward_ws, gpu_forward, require_gpu, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -96,11 +96,13 @@ def test_forward_quantize_x(cfg):
     print(f"forward with quantised x: T={cfg.T} E={cfg.E} k={cfg.k} H={cfg.H} I={cfg.I}", flush=True)
     inp = synth.make_moe_inputs(cfg)
     d = to_dev(inp)
-    f32 = gpu_forward(inp, d, out_dtype=torch.float32, quantize_x=True)
+    f32, ws, p = forward_ws(inp, d, quantize_x=True)
     b16 = gpu_forward(inp, d, quantize_x=True)
     torch.cuda.synchronize()
     assert torch.equal(f32.to(torch.bfloat16).view(torch.int16), b16.view(torch.int16))
     codes, sf = _quant_inputs(inp)
-    ref, band = oracle.moe_forward(codes, inp.topk_ids, inp.topk_w, inp.w13, inp.w13_sf, inp.w13_gs,
-                                   inp.w2, inp.w2_sf, inp.w2_gs, cfg.gran, x_sf=sf, return_band=True)
+    ref, band, hrows = oracle.moe_forward(codes, inp.topk_ids, inp.topk_w, inp.w13, inp.w13_sf, inp.w13_gs,
+                                          inp.w2, inp.w2_sf, inp.w2_gs, cfg.gran, x_sf=sf, return_band=True,
+                                          return_h=True)
+    check_h(ws, p, hrows, "quantised-x forward")
     check_bound(f32.cpu().numpy().astype(np.float64), ref, "quantised-x forward", band)

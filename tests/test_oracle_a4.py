@@ -58,13 +58,13 @@ def test_quantize_a4_brute_force():
 
 def test_decision_band_a4():
     """Block max 1.4 (e = -2, scaled grid step 0.5 below 2): scaled 1.25 is a
-    midpoint, within the radius 1.4 * 2**-14 of it the band is one step, away
+    midpoint, within the radius 1.4 * 2**-17 of it the band is one step, away
     from it zero; a block maximum on 6 * 2**e spans both exponents."""
     h = np.zeros((1, 32))
     h[0, 0] = 1.4
     h[0, 1] = 1.25 * 0.25                    # scaled 1.25: midpoint of 1 and 1.5
-    h[0, 2] = 1.25 * 0.25 + 2.0 ** -19       # within 1.4 * 2**-14 of it
-    h[0, 3] = 1.25 * 0.25 + 2.0 ** -12       # outside
+    h[0, 2] = 1.25 * 0.25 + 2.0 ** -19       # within 1.4 * 2**-17 of it
+    h[0, 3] = 1.25 * 0.25 + 2.0 ** -15       # outside
     band = oracle.h_decision_band(h, False, a4=True)
     assert band[0, 1] == 0.5 * 0.25 and band[0, 2] == 0.5 * 0.25
     assert band[0, 3] == 0 and band[0, 0] == 0

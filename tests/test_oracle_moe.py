@@ -11,6 +11,7 @@ import torch
 
 import oracle
 import synth
+from oracle.moe import decode_activations
 
 
 def test_route_matches_stable_argsort():
@@ -256,14 +257,16 @@ def test_decision_band():
     """The band is one grid step exactly for values within the radius (times
     the block maximum) of a rounding midpoint, zero elsewhere, and covers the
     neighbouring exponent when a block maximum sits on 448 * 2**e."""
-    # bf16, block max 4: radius 4 * 2**-14 = 2**-12.  1 + 2**-8 is a midpoint
-    # (step 2**-7); 1 + 2**-8 + 2**-13 is within the radius, + 2**-11 is not
+    assert oracle.decision_radius(False) == 2.0 ** -17 and oracle.decision_radius(True, a4=True) == 2.0 ** -17
+    assert oracle.decision_radius(True) == 2.0 ** -13
+    # bf16, block max 4: radius 4 * 2**-17 = 2**-15.  1 + 2**-8 is a midpoint
+    # (step 2**-7); 1 + 2**-8 + 2**-16 is within the radius, + 2**-14 is not
     h = np.zeros((1, 32))
-    h[0, :5] = [1.0 + 2.0 ** -8, 1.0 + 2.0 ** -8 + 2.0 ** -13, 1.0 + 2.0 ** -8 + 2.0 ** -11,
+    h[0, :5] = [1.0 + 2.0 ** -8, 1.0 + 2.0 ** -8 + 2.0 ** -16, 1.0 + 2.0 ** -8 + 2.0 ** -14,
                 1.0 + 2.0 ** -9, 4.0]
     b = oracle.h_decision_band(h, a8=False)
     assert list(b[0, :5]) == [2.0 ** -7, 2.0 ** -7, 0.0, 0.0, 0.0] and not b[0, 5:].any()
-    # E4M3, block max 300 (e = 0, radius 300 * 2**-14 ~ 0.018): the midpoint
+    # E4M3, block max 300 (e = 0, FP8 radius 300 * 2**-13 ~ 0.037): the midpoint
     # 1 + 2**-4 is ambiguous by one step (0.125); 2.3 is clear; a value in the
     # subnormal range is ambiguous by its quantum 2**-9 (its half-step is
     # smaller than the radius)
@@ -278,3 +281,83 @@ def test_decision_band():
     prim = oracle.quantize_h_a8(blk)[0]
     alt = np.ldexp(oracle.e4m3_decode(oracle.rne_e4m3(blk / 2.0)), 1)
     assert np.all(b >= np.abs(alt - prim)) and np.any(alt != prim)
+
+
+def _seq_fp32_h_distance(cfg, rows, toks, experts):
+    """Largest |h32 - h| / (block max of |h|) over the first `toks` tokens and
+    the first `rows` gate rows (with their up rows) of the first `experts`
+    experts: h exact (FP64), h32 from an FP32 emulation of the kernels'
+    arithmetic -- exact products, each added to an FP32 sum in sequence (the
+    most roundings any accumulation order takes), the global scale applied
+    to the FP32 sum, SwiGLU in FP32."""
+    inp = synth.make_moe_inputs(cfg)
+    xv = decode_activations(inp.x, inp.x_sf)
+    kind = {16: "e4m3", 32: "ue8m0"}[cfg.gran]
+    sel = np.r_[0:rows, cfg.I:cfg.I + rows]
+    worst = 0.0
+    for e in range(experts):
+        W = oracle.dequant_fp4(inp.w13[e][sel], inp.w13_sf[e][sel], cfg.gran, kind, None)
+        gs = 1.0 if inp.w13_gs is None else float(inp.w13_gs[e])
+        X = xv[:toks]
+        P = X[:, None, :] * W[None, :, :]
+        P32 = P.astype(np.float32)
+        assert np.array_equal(P32.astype(np.float64), P), "FC1 products are exact in FP32"
+        G = (X @ W.T) * gs
+        G32 = np.add.accumulate(P32, axis=2, dtype=np.float32)[..., -1] * np.float32(gs)
+        h = oracle.silu(G[:, :rows]) * G[:, rows:]
+        g3, u3 = G32[:, :rows], G32[:, rows:]
+        h32 = (g3 / (np.float32(1) + np.exp(-g3)) * u3).astype(np.float64)
+        bmax = np.abs(h).reshape(toks, rows // 32, 32).max(axis=-1)
+        d = np.abs(h32 - h).reshape(toks, rows // 32, 32) / bmax[..., None]
+        worst = max(worst, float(d.max()))
+    return worst
+
+
+@pytest.mark.parametrize("name", ["decode16", "decode32", "prefill_bf16_g32", "tiny"])
+def test_decision_radius_covers_fp32(name):
+    """The decision radius (2**-17 of the block maximum) is at least four times
+    the distance between the exact h and an FP32 computation of it in the
+    order with the most roundings, on the workloads' shapes (K = 6144 for
+    the GLM-sized layers)."""
+    cfg = {"decode16": synth.variant(synth.CONFIGS["decode16"], T=8, E=2),
+           "decode32": synth.variant(synth.CONFIGS["decode32"], T=8, E=2),
+           "prefill_bf16_g32": synth.variant(synth.CONFIGS["decode32"], T=8, E=2, act="bf16"),
+           "tiny": synth.CONFIGS["tiny"]}[name]
+    rows = 128 if name == "tiny" else 192
+    d = _seq_fp32_h_distance(cfg, rows=rows, toks=8, experts=2)
+    print(f"{name}: max |h32 - h| = 2**{np.log2(d):.2f} of the block max", flush=True)
+    assert d <= oracle.moe.DECISION_RADIUS / 4
+
+
+def test_decision_margin():
+    """The margin is the distance to the nearest rounding midpoint (or block
+    exponent boundary) over the block maximum; it is within the radius exactly
+    where the band is nonzero on the grid cases."""
+    h = np.zeros((1, 32))
+    h[0, :5] = [1.0 + 2.0 ** -8, 1.0 + 2.0 ** -8 + 2.0 ** -13, 1.0, 3.0 + 2.0 ** -7, 4.0]
+    m = oracle.h_decision_margin(h, a8=False)
+    # midpoint; 2**-13 from it; on the grid (half a step 2**-8 from the
+    # midpoints); 3 + 2**-7 is the midpoint of 3 and 3 + 2**-6; the maximum 4
+    # sits on the grid, half a step 2**-6 from the midpoints
+    assert m[0, 0] == 0.0 and m[0, 1] == 2.0 ** -15 and m[0, 2] == 2.0 ** -10
+    assert m[0, 3] == 0.0 and m[0, 4] == 2.0 ** -6 / 4
+    b = oracle.h_decision_band(h, a8=False)
+    assert np.array_equal(b != 0, m <= oracle.moe.DECISION_RADIUS)
+    # E4M3, block max 300 (e = 0): 1 + 2**-4 is a midpoint; 2.3 is 0.075 from
+    # the midpoint 2.375 of 2.25 and 2.5; 300 lies 4 from the midpoint 304 of
+    # 288 and 320 (its
+    # exponent boundaries 224 and 448 are farther)
+    blk = np.zeros((1, 32))
+    blk[0, :3] = [300.0, 1.0 + 2.0 ** -4, 2.3]
+    m = oracle.h_decision_margin(blk, a8=True)
+    assert m[0, 1] == 0.0
+    assert np.isclose(m[0, 2], 0.075 / 300, rtol=1e-12)
+    assert m[0, 0] == 4.0 / 300
+    # a block maximum on the exponent boundary: every element has margin 0
+    blk[0, 0] = 448.0
+    assert np.all(oracle.h_decision_margin(blk, a8=True)[0] == 0.0)
+    # A4: block max 1.4 (e = -2: scaled 5.6), scaled 1.25 is a midpoint
+    h4 = np.zeros((1, 32))
+    h4[0, :2] = [1.4, 1.25 * 0.25]
+    m4 = oracle.h_decision_margin(h4, False, a4=True)
+    assert m4[0, 1] == 0.0 and m4[0, 0] > 0
