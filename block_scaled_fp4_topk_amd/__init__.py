@@ -11,6 +11,7 @@ Functions mirror the C entry points:
   workspace_offsets(problem)          -> moe_fp4_workspace_offsets
   route(problem, topk_ids, ...)       -> moe_fp4_route
   forward(x, topk_ids, topk_w, ...)   -> moe_fp4_forward
+  forward_static(x, topk_ids, ...)    -> moe_fp4_forward_static (no workspace)
   requant_gran_k(src, src_sf, ...)    -> fp4_requant_gran_k
   prepare_gemm_weights(src, src_sf, ...) -> moe_fp4_prepare_gemm_weights
   prepare_gemm_weights_g16(src, src_sf, src_gs, ...) -> moe_fp4_prepare_gemm_weights_g16
@@ -24,7 +25,7 @@ import ctypes
 import os
 
 __all__ = ["Problem", "MoeFp4Error", "lib", "workspace_bytes", "workspace_offsets", "route", "forward",
-           "forward_problem",
+           "forward_problem", "forward_static",
            "requant_gran_k", "prepare_gemm_weights", "prepare_gemm_weights_g16", "quantize_act", "quantize_act_fp4",
            "dropped_assignments", "LIB_PATH"]
 
@@ -72,6 +73,9 @@ def lib():
         L.moe_fp4_forward.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                       _P, _P, ctypes.c_size_t, _P]
         L.moe_fp4_forward.restype = st
+        L.moe_fp4_forward_static.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                             _P, _P]
+        L.moe_fp4_forward_static.restype = st
         L.fp4_requant_gran_k.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _P, _P,
                                          ctypes.c_int32, _P, _P, _P, ctypes.c_int32, _P]
         L.fp4_requant_gran_k.restype = st
@@ -238,6 +242,35 @@ def forward(x, topk_ids, topk_w, w13, w13_sf, w13_gs, w2, w2_sf, w2_gs, gran_k, 
     _check(lib().moe_fp4_forward(ctypes.byref(p), _ptr(x), _ptr(x_sf), _ptr(topk_ids), _ptr(topk_w),
                                  _ptr(w13), _ptr(w13_sf), _ptr(w13_gs), _ptr(w2), _ptr(w2_sf),
                                  _ptr(w2_gs), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def forward_static(x, topk_ids, topk_w, w13, w13_sf, w13_gs, w2, w2_sf, w2_gs, gran_k, x_sf=None,
+                   w13_order="gate_up", out=None, stream=None, out_dtype=None, quantize_x=False, w_layout="raw"):
+    """forward() without a workspace: moe_fp4_forward_static, whose
+    workspace is the library's static device scratch (64 MiB per GPU; larger
+    problems raise with status EWORKSPACE).  Calls that overlap on one GPU
+    race; calls on one stream are ordered."""
+    import torch
+    u8 = (torch.uint8,)
+    a8 = x_sf is not None
+    _dev(x, "x", (torch.uint8, torch.float8_e4m3fn) if a8 else (torch.bfloat16, torch.int16, torch.uint16))
+    _dev(x_sf, "x_sf", u8)
+    _dev(topk_ids, "topk_ids", (torch.int32,))
+    _dev(topk_w, "topk_w", (torch.float32,))
+    for n, t in (("w13", w13), ("w13_sf", w13_sf), ("w2", w2), ("w2_sf", w2_sf)):
+        _dev(t, n, u8)
+    _dev(w13_gs, "w13_gs", (torch.float32,))
+    _dev(w2_gs, "w2_gs", (torch.float32,))
+    if out_dtype is None:
+        out_dtype = torch.bfloat16 if out is None else out.dtype
+    p = forward_problem(x, topk_ids, w13, w2, gran_k, x_sf, w13_order, out_dtype, quantize_x, w_layout)
+    if out is None:
+        out = torch.empty((p.T, p.H), dtype=out_dtype, device=x.device)
+    _dev(out, "out", (out_dtype,))
+    _check(lib().moe_fp4_forward_static(ctypes.byref(p), _ptr(x), _ptr(x_sf), _ptr(topk_ids), _ptr(topk_w),
+                                        _ptr(w13), _ptr(w13_sf), _ptr(w13_gs), _ptr(w2), _ptr(w2_sf),
+                                        _ptr(w2_gs), _ptr(out), _stream(stream)))
     return out
 
 

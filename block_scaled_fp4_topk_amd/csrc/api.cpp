@@ -7,6 +7,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "../../include/moefp4.h"
@@ -186,6 +187,41 @@ moefp4_status route_into(const moefp4_problem* p, const Layout& L, const int32_t
   return hip_status(moefp4::launch_route(ids, p->T * p->top_k, p->E, L.tile_m, o, s), "route");
 }
 
+// The scratch of moe_fp4_forward_static: a file-scope device array, one copy
+// per GPU, that holds the forward's workspace for callers that cannot
+// allocate.  Host code uses only the per-device address hipGetSymbolAddress
+// returns for it (the array's name is not a device address on the host).
+constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
+
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// This device's copy of the scratch array (resolved once per device, with
+// that device current).
+moefp4_status static_scratch(void** ptr) {
+  int dev = -1;
+  moefp4_status st = hip_status(hipGetDevice(&dev), "hipGetDevice");
+  if (st != MOEFP4_OK) return st;
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOEFP4_EUNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    st = hip_status(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (st != MOEFP4_OK) return st;
+    if (!p) return fail(MOEFP4_EHIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return MOEFP4_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -355,6 +391,24 @@ moefp4_status moe_fp4_forward(const moefp4_problem* p, const void* x, const uint
   if (st != MOEFP4_OK) return st;
   if ((st = stage_mark(5, stream)) != MOEFP4_OK) return st;
   return ok();
+}
+
+moefp4_status moe_fp4_forward_static(const moefp4_problem* p, const void* x, const uint8_t* x_sf,
+                                     const int32_t* topk_ids, const float* topk_w, const uint8_t* w13,
+                                     const uint8_t* w13_sf, const float* w13_gs, const uint8_t* w2,
+                                     const uint8_t* w2_sf, const float* w2_gs, void* out, hipStream_t stream) {
+  Layout L;
+  moefp4_status st = plan(p, &L);
+  if (st != MOEFP4_OK) return st;
+  if (L.total > kStaticScratchBytes)
+    return fail(MOEFP4_EWORKSPACE,
+                "this problem needs %zu bytes of scratch; the static scratch of moe_fp4_forward_static holds %zu "
+                "(use moe_fp4_forward with a caller workspace)",
+                L.total, kStaticScratchBytes);
+  void* ws = nullptr;
+  if ((st = static_scratch(&ws)) != MOEFP4_OK) return st;
+  return moe_fp4_forward(p, x, x_sf, topk_ids, topk_w, w13, w13_sf, w13_gs, w2, w2_sf, w2_gs, out, ws,
+                         kStaticScratchBytes, stream);
 }
 
 moefp4_status fp4_requant_gran_k(int64_t E, int64_t N, int64_t K, const uint8_t* src,

@@ -167,6 +167,27 @@ moefp4_status moe_fp4_forward(const moefp4_problem* p,
                               void* out, void* workspace, size_t ws_bytes,
                               hipStream_t stream);
 
+/* moe_fp4_forward without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): the workspace is a static device
+ * array inside the library, 64 MiB per GPU (held from the library's load
+ * until the process ends), which covers decode-sized problems (e.g. 256
+ * tokens, top-8, H = 6144, I = 2048 needs about 56 MiB); a problem whose
+ * workspace (moe_fp4_workspace_bytes) exceeds it returns MOEFP4_EWORKSPACE
+ * with a message and enqueues nothing.  Arguments, layouts, supported
+ * problems and errors otherwise as moe_fp4_forward; the result is bit-
+ * identical to moe_fp4_forward's.  No allocation, no synchronisation.
+ * Every call on one GPU uses that GPU's one array: calls that overlap on a
+ * GPU (concurrent streams, or threads) race and must be serialised by the
+ * caller; stream-ordered calls on one stream are safe.  The dropped-id count
+ * of moe_fp4_workspace_bytes lands in the static array and is not reported. */
+moefp4_status moe_fp4_forward_static(const moefp4_problem* p,
+                                     const void* x, const uint8_t* x_sf,
+                                     const int32_t* topk_ids, const float* topk_w,
+                                     const uint8_t* w13, const uint8_t* w13_sf, const float* w13_gs,
+                                     const uint8_t* w2, const uint8_t* w2_sf, const float* w2_gs,
+                                     void* out, hipStream_t stream);
+
 /* Reorder group32 weights (RAW layout, UE8M0 scales) into the GEMM layout
  * of the prefill kernels.  which = 0: w13 (N = 2I rows in w13_order, K =
  * H); which = 1: w2 (N = H, K = I).  The GEMM's weight rows are taken in
