@@ -62,6 +62,10 @@ class HipEvents:
             if self.hip.hipEventCreate(ctypes.byref(self.arr, i * ctypes.sizeof(ctypes.c_void_p))) != 0:
                 raise RuntimeError("hipEventCreate failed")
 
+    def record(self, i, stream):
+        if self.hip.hipEventRecord(ctypes.c_void_p(self.arr[i]), ctypes.c_void_p(stream.cuda_stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
     def sub(self, i0, n):
         return ctypes.cast(ctypes.byref(self.arr, i0 * ctypes.sizeof(ctypes.c_void_p)),
                            ctypes.POINTER(ctypes.c_void_p))
@@ -101,22 +105,25 @@ def to_dev(torch, inp):
     return d
 
 
+def alloc_forward(moe, torch, inp):
+    """The workspace and output of a forward on this workload (no launch)."""
+    c = inp.cfg
+    p = moe.make_problem(c.T, c.E, c.k, c.H, c.I, c.gran,
+                         {"fp8": moe.ACT_FP8_UE8M0_K32,
+                          "bf16q": moe.ACT_BF16_QUANT_FP8_K32,
+                          "bf16q4": moe.ACT_BF16_QUANT_FP4_K32}.get(c.act, moe.ACT_BF16),
+                         w_layout="gemm" if c.name.endswith("_prep") else "raw")
+    ws = torch.empty(moe.workspace_bytes(p), dtype=torch.uint8, device="cuda")
+    out = torch.empty((c.T, c.H), dtype=torch.bfloat16, device="cuda")
+    return ws, out
+
+
 def gpu_forward_into(moe, torch, inp, d, ws, out):
-    """One forward; allocates the workspace and output on the first call."""
-    if ws is None:
-        c = inp.cfg
-        p = moe.make_problem(c.T, c.E, c.k, c.H, c.I, c.gran,
-                             {"fp8": moe.ACT_FP8_UE8M0_K32,
-                              "bf16q": moe.ACT_BF16_QUANT_FP8_K32,
-                              "bf16q4": moe.ACT_BF16_QUANT_FP4_K32}.get(c.act, moe.ACT_BF16),
-                             w_layout="gemm" if c.name.endswith("_prep") else "raw")
-        ws = torch.empty(moe.workspace_bytes(p), dtype=torch.uint8, device="cuda")
-        out = torch.empty((c.T, c.H), dtype=torch.bfloat16, device="cuda")
+    """One forward into the given workspace and output."""
     moe.forward(d["x"], d["topk_ids"], d["topk_w"], d["w13"], d["w13_sf"], d["w13_gs"], d["w2"],
                 d["w2_sf"], d["w2_gs"], inp.cfg.gran, x_sf=d["x_sf"], out=out, workspace=ws,
                 quantize_x={"bf16q": "fp8", "bf16q4": "fp4"}.get(inp.cfg.act, False),
                 w_layout="gemm" if inp.cfg.name.endswith("_prep") else "raw")
-    return ws, out
 
 
 def stage_kernel(cfg, ids, stage):
@@ -209,11 +216,13 @@ def pmc_traffic(kernel_key, workload):
 
 
 def run_forward_timed(moe, torch, inp, d, steps, warmup):
-    """Warm up, then time `steps` forwards (synchronised on both sides) with no
-    instrumentation; then `steps` more with per-stage HIP events recorded by
-    the library on the launch stream (for the per-kernel durations: an event
-    record between two kernels adds a few microseconds of its own)."""
-    ws, out = gpu_forward_into(moe, torch, inp, d, None, None)
+    """Exactly `warmup` untimed forwards, then `steps` forwards timed by the
+    wall clock with no instrumentation (synchronised on both sides: the
+    headline); then `steps` forwards with one HIP event at each step boundary
+    on the launch stream (per-step durations: median and mean); then `steps`
+    with per-stage events recorded by the library (an event record between
+    two kernels adds a few microseconds of its own)."""
+    ws, out = alloc_forward(moe, torch, inp)
     for _ in range(warmup):
         gpu_forward_into(moe, torch, inp, d, ws, out)
     torch.cuda.synchronize()
@@ -222,6 +231,14 @@ def run_forward_timed(moe, torch, inp, d, steps, warmup):
         gpu_forward_into(moe, torch, inp, d, ws, out)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    stream = torch.cuda.current_stream()
+    be = HipEvents(steps + 1)
+    for i in range(steps):
+        be.record(i, stream)
+        gpu_forward_into(moe, torch, inp, d, ws, out)
+    be.record(steps, stream)
+    torch.cuda.synchronize()
+    per_step = np.array([be.ms(i, i + 1) for i in range(steps)])
     ev = HipEvents(6 * steps)
     for i in range(steps):
         moe.set_stage_events(ev.sub(6 * i, 6), 6)
@@ -230,40 +247,103 @@ def run_forward_timed(moe, torch, inp, d, steps, warmup):
     moe.set_stage_events(None, 0)
     stage_ms = {name: float(np.mean([ev.ms(6 * i + s, 6 * i + s + 1) for i in range(steps)]))
                 for s, name in enumerate(STAGES)}
-    fwd_ms = float(np.mean([ev.ms(6 * i, 6 * i + 5) for i in range(steps)]))
-    return (t1 - t0) * 1e3 / steps, fwd_ms, stage_ms
+    return {"wall_ms": (t1 - t0) * 1e3 / steps, "event_median_ms": float(np.median(per_step)),
+            "event_mean_ms": float(np.mean(per_step)), "stage_ms": stage_ms}
+
+
+_CPU_INP = None  # the workload the oracle workers read (inherited through fork)
+
+
+def _oracle_token(t):
+    inp = _CPU_INP
+    import oracle
+    oracle.moe_forward(inp.x, inp.topk_ids, inp.topk_w, inp.w13, inp.w13_sf, inp.w13_gs,
+                       inp.w2, inp.w2_sf, inp.w2_gs, inp.cfg.gran, x_sf=inp.x_sf, tokens=[t])
+    return t
+
+
+def _one_blas_thread():
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except Exception:  # noqa: BLE001
+        pass
 
 
 def cpu_baseline(inp, budget_s=15.0):
-    """The FP64 oracle as it stands, on this host, on a bounded sample of the
-    same workload: whole tokens (all their experts, all H outputs) until about
-    budget_s seconds of work; tokens/s = tokens done / time."""
-    import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        blas = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # noqa: BLE001
-        blas = 1
-    done, t0 = 0, time.perf_counter()
-    while time.perf_counter() - t0 < budget_s and done < inp.cfg.T:
-        oracle.moe_forward(inp.x, inp.topk_ids, inp.topk_w, inp.w13, inp.w13_sf, inp.w13_gs,
-                           inp.w2, inp.w2_sf, inp.w2_gs, inp.cfg.gran, x_sf=inp.x_sf,
-                           tokens=[done])
-        done += 1
-    dt = time.perf_counter() - t0
-    return {"value": done / dt, "unit": "tokens/s", "cores": blas, "kind": "oracle",
-            "sample": f"{done} whole token(s) of the {inp.cfg.name} workload (all {inp.cfg.k} experts, "
-                      f"all {inp.cfg.H} outputs), {dt:.1f} s; numpy FP64, BLAS threads={blas}, "
-                      f"elementwise work single-threaded"}
+    """The FP64 oracle as it stands, on this host's cores, on a bounded sample
+    of the same workload: a process pool over tokens (each token's k experts
+    and all H outputs; N = the CPUs this process may run on, at most 16, the
+    host share of one GPU; one BLAS thread per worker) until about budget_s
+    seconds or every token; tokens/s = tokens done / wall time.  Runs before
+    the GPU is initialised (the workers are forked)."""
+    import multiprocessing as mp
+    global _CPU_INP
+    _CPU_INP = inp
+    n = max(1, min(len(os.sched_getaffinity(0)), 16))
+    finished = []
+    with mp.get_context("fork").Pool(n, initializer=_one_blas_thread) as pool:
+        t0 = time.perf_counter()
+        for t in range(inp.cfg.T):
+            pool.apply_async(_oracle_token, (t,), callback=lambda _: finished.append(time.perf_counter()))
+        # until the budget is spent (and at least one token per worker, or
+        # every token, has finished)
+        while len(finished) < inp.cfg.T and (time.perf_counter() - t0 < budget_s
+                                             or len(finished) < min(n, inp.cfg.T)):
+            time.sleep(0.05)
+        ends = sorted(finished)
+        pool.terminate()
+    done, dt = len(ends), ends[-1] - t0
+    _CPU_INP = None
+    return {"value": done / dt, "unit": "tokens/s", "cores": n, "kind": "oracle",
+            "sample": f"{done} of the {inp.cfg.T} tokens of the {inp.cfg.name} workload (each with its "
+                      f"{inp.cfg.k} experts and all {inp.cfg.H} outputs) in {dt:.1f} s; numpy FP64, a pool of "
+                      f"{n} processes over tokens, one BLAS thread each"}
+
+
+def measured_peaks(moe, torch):
+    """What this GPU delivers, beside the published peaks: a 1 GiB device
+    copy (read + write bytes / time) and the register-only loop of the
+    block-scaled MFMA with FP4 x FP8 and FP4 x FP4 operands (best of 3
+    HIP-event timings each)."""
+    a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = 1e30
+    for _ in range(5):
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1))
+    copy_gbs = 2 * (1 << 30) / (best * 1e-3) / 1e9
+    del a, b
+    blocks = 2048
+    sink = torch.zeros(blocks * 256, dtype=torch.float32, device="cuda")
+    res = {"copy_GBps": copy_gbs}
+    for name, a4 in (("mfma_fp4xfp8_TFLOPs", False), ("mfma_fp4xfp4_TFLOPs", True)):
+        moe.mfma_peak_probe(a4, 200, blocks, sink)
+        best, fl = 1e30, 0.0
+        for _ in range(3):
+            e0.record()
+            fl = moe.mfma_peak_probe(a4, 2000, blocks, sink)
+            e1.record()
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1))
+        res[name] = fl / (best * 1e-3) / 1e12
+    del sink
+    torch.cuda.empty_cache()
+    return res
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    # the first ~50 ms of back-to-back forwards after idle run up to 10%
-    # slower (measured on MI355X: 0.87 -> 0.79 ms per decode16 step over the
-    # first four groups of 20 steps), so the default warmup covers ~80 ms
+    # the first ~30 forwards after the GPU has been idle (even 0.5 s) run up
+    # to 20% slower (decode16 on MI355X: 0.99, 0.92, 0.86, 0.83 ms per step
+    # over the first four groups of 10, then 0.82), so the default warmup
+    # covers ~80 ms
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="decode16", choices=list(WORKLOAD_TEXT))
     ap.add_argument("--no-secondary", action="store_true")
@@ -283,12 +363,14 @@ def main():
     import torch
     import block_scaled_fp4_topk_amd as moe
     import synth
-    if not torch.cuda.is_available():
+    # (device_count does not initialise the GPU: the CPU baseline's workers
+    # are forked before anything touches it)
+    if torch.cuda.device_count() < 1:
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
-    moe.lib()  # fails loudly if the HIP library is not built
 
     if args.requant_only:
+        moe.lib()  # fails loudly if the HIP library is not built
         print("[bench] generating decode16 weights", file=sys.stderr, flush=True)
         inp16 = synth.make_moe_inputs(workload_cfg(synth, "decode16"))
         print("[bench] timing requant", file=sys.stderr, flush=True)
@@ -300,11 +382,17 @@ def main():
     cfg = workload_cfg(synth, args.workload)
     print(f"[bench] generating {cfg.name} inputs", file=sys.stderr, flush=True)
     inp = synth.make_moe_inputs(cfg)
+    cpu = None
+    if not args.no_cpu_baseline and not args.profile:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(inp)
+    moe.lib()  # fails loudly if the HIP library is not built
     d = to_dev(torch, inp)
     if cfg.name.endswith("_prep"):
         prepare_weights(moe, torch, d)
     print("[bench] timing", file=sys.stderr, flush=True)
-    ms_step, fwd_ms, stage_ms = run_forward_timed(moe, torch, inp, d, args.steps, args.warmup)
+    tm = run_forward_timed(moe, torch, inp, d, args.steps, args.warmup)
+    ms_step, stage_ms = tm["wall_ms"], tm["stage_ms"]
     ab = algorithmic_bytes(cfg, inp.topk_ids)
     dom = max(("fc1_swiglu", "fc2"), key=lambda s: stage_ms[s])
     dom_bytes = ab["fc1"] if dom == "fc1_swiglu" else ab["fc2"]
@@ -331,21 +419,29 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": pmc_traffic(kernel_key, cfg.name),
                      "algorithmic_bytes_per_launch": dom_bytes, "launch_ms": stage_ms[dom]},
-        # whole forward from the uninstrumented steps; event_ms is the
-        # instrumented forward (stage events add a few us per stage)
-        "forward": {"ms": ms_step, "event_ms": fwd_ms, "stage_ms": stage_ms,
+        # ms: the uninstrumented timed steps (wall clock, the headline);
+        # event_median_ms / event_mean_ms: per-step HIP events at the step
+        # boundaries over as many further steps; stage_ms: per-stage events
+        "forward": {"ms": ms_step, "event_median_ms": tm["event_median_ms"],
+                    "event_mean_ms": tm["event_mean_ms"], "stage_ms": stage_ms,
                     "algorithmic_bytes": ab["whole"],
                     "achieved_GBps": ab["whole"] / (ms_step * 1e-3) / 1e9,
                     "hbm_frac": ab["whole"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                    "hbm_frac_event_median": ab["whole"] / (tm["event_median_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
                     "tflops": flops(cfg) / (ms_step * 1e-3) / 1e12},
     }
     if args.profile:
         res["copy_calibration_bytes"] = copy_calibration(torch)
-    if not args.no_cpu_baseline and not args.profile:
-        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(inp)
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
     if not args.no_secondary and not args.profile:
-        res["secondary"] = secondary(moe, torch, synth, args, inp, d)
+        print("[bench] measured peaks", file=sys.stderr, flush=True)
+        pk = measured_peaks(moe, torch)
+        res["measured_peaks"] = dict(pk, copy_frac_of_8TBps=pk["copy_GBps"] / HBM_PEAK_GBS,
+                                     mfma_fp4xfp8_frac_of_5PF=pk["mfma_fp4xfp8_TFLOPs"] / PEAK_TFLOPS["fp8"],
+                                     mfma_fp4xfp4_frac_of_10_1PF=pk["mfma_fp4xfp4_TFLOPs"] / PEAK_TFLOPS["fp4"])
+        res["roofline"]["frac_of_measured_copy"] = achieved / pk["copy_GBps"]
+        res["secondary"] = secondary(moe, torch, synth, args, inp, d, pk)
     print(json.dumps(res), flush=True)
 
 
@@ -399,8 +495,24 @@ def requant_layer(moe, torch, inp16):
     return res
 
 
-def secondary(moe, torch, synth, args, inp16, d16):
-    """The other workloads of the hot path, each timed the same way."""
+def gemm_counters(kernel_key, workload):
+    """MFMA busy and issued / algorithmic MFMA counts of a prefill GEMM
+    kernel from the committed rocprofv3 --pmc summary, if it was taken on the
+    current kernel sources; else None."""
+    p = os.path.join(ROOT, "profiles", f"{kernel_key}_{workload}_pmc.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        d = json.load(f)
+    if d.get("source_hash") != kernel_source_hash():
+        return None
+    return {k: d[k] for k in ("mfma_busy", "mfmas_issued", "mfmas_algorithmic", "fetch_over_algorithmic")
+            if k in d}
+
+
+def secondary(moe, torch, synth, args, inp16, d16, peaks):
+    """The other workloads of the hot path, each timed the same way; the
+    prefill ones with the MFMA roofline of their FC1 GEMM."""
     out = {}
     del d16
     torch.cuda.empty_cache()
@@ -414,16 +526,26 @@ def secondary(moe, torch, synth, args, inp16, d16):
         if name.endswith("_prep"):
             prepare_weights(moe, torch, d)
         steps, warm = (10, 10) if name.startswith("prefill") else (50, 100)
-        ms_step, fwd_ms, stage_ms = run_forward_timed(moe, torch, inp, d, steps, warm)
+        tm = run_forward_timed(moe, torch, inp, d, steps, warm)
+        ms_step, stage_ms = tm["wall_ms"], tm["stage_ms"]
         ab = algorithmic_bytes(cfg, inp.topk_ids)
         r = {"workload": WORKLOAD_TEXT[name], "ms_per_step": ms_step, "tokens_per_s": cfg.T / (ms_step * 1e-3),
+             "event_median_ms": tm["event_median_ms"],
              "stage_ms": stage_ms, "algorithmic_bytes": ab["whole"],
              "hbm_frac": ab["whole"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
              "tflops": flops(cfg) / (ms_step * 1e-3) / 1e12}
-        if cfg.act == "bf16q4":
-            r["mfma_frac_fp4_peak"] = r["tflops"] / PEAK_TFLOPS["fp4"]
-        else:
-            r["mfma_frac_fp8_peak"] = r["tflops"] / PEAK_TFLOPS["fp8"]
+        a4 = cfg.act == "bf16q4"
+        peak = PEAK_TFLOPS["fp4" if a4 else "fp8"]
+        r["mfma_frac_fp4_peak" if a4 else "mfma_frac_fp8_peak"] = r["tflops"] / peak
+        if name.startswith("prefill"):
+            kern = stage_kernel(cfg, inp.topk_ids, "fc1_swiglu")
+            fl1 = 2.0 * cfg.T * cfg.k * 2 * cfg.I * cfg.H
+            ach = fl1 / (stage_ms["fc1_swiglu"] * 1e-3) / 1e12
+            meas = peaks["mfma_fp4xfp4_TFLOPs" if a4 else "mfma_fp4xfp8_TFLOPs"]
+            r["roofline"] = {"bound": "mfma", "kernel": kern, "achieved": ach, "peak": peak, "unit": "TFLOP/s",
+                             "frac": ach / peak, "measured_peak": meas, "frac_of_measured_peak": ach / meas,
+                             "algorithmic_flops_per_launch": fl1, "launch_ms": stage_ms["fc1_swiglu"],
+                             "counters": gemm_counters(kernel_file_key(kern), name)}
         out[name] = r
         del d
         torch.cuda.empty_cache()

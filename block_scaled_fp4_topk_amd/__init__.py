@@ -91,6 +91,9 @@ def lib():
         L.moe_fp4_quantize_act_fp4.restype = st
         L.moefp4_last_error.argtypes = []
         L.moefp4_last_error.restype = ctypes.c_char_p
+        L.moefp4_mfma_peak_probe.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P,
+                                             ctypes.POINTER(ctypes.c_double), _P]
+        L.moefp4_mfma_peak_probe.restype = st
         L.moefp4_set_stage_events.argtypes = [_P, ctypes.c_int32]
         L.moefp4_set_stage_events.restype = st
         L.moefp4_version.argtypes = []
@@ -371,6 +374,16 @@ def quantize_act(x, x_fp8=None, x_sf=None, stream=None):
     _dev(x_sf, "x_sf", (torch.uint8,))
     _check(lib().moe_fp4_quantize_act(T, H, _ptr(x), _ptr(x_fp8), _ptr(x_sf), _stream(stream)))
     return x_fp8, x_sf
+
+
+def mfma_peak_probe(a4: bool, iters: int, blocks: int, sink, stream=None) -> float:
+    """Enqueue the register-only block-scaled MFMA loop (moefp4_mfma_peak_probe);
+    returns the flops it performs.  sink: float32 CUDA tensor of blocks*256."""
+    import torch
+    _dev(sink, "sink", (torch.float32,))
+    f = ctypes.c_double(0)
+    _check(lib().moefp4_mfma_peak_probe(1 if a4 else 0, iters, blocks, _ptr(sink), ctypes.byref(f), _stream(stream)))
+    return f.value
 
 
 def set_stage_events(events_array, n: int):

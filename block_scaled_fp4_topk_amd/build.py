@@ -20,7 +20,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoefp4.so")
-SOURCES = ["api.cpp", "route.hip", "moe_a16.hip", "moe_a8.hip", "moe_decode.hip", "moe_gemm.hip", "requant.hip"]
+SOURCES = ["api.cpp", "route.hip", "moe_a16.hip", "moe_a8.hip", "moe_decode.hip", "moe_gemm.hip", "requant.hip",
+           "diag.hip"]
 ARCH = os.environ.get("MOEFP4_ARCH", "gfx950")
 
 

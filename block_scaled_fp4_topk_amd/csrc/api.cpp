@@ -329,63 +329,56 @@ moefp4_status moe_fp4_forward(const moefp4_problem* p, const void* x, const uint
     a.act = L.quant_x ? x8 : x;
     a.act_sf = L.quant_x ? x8_sf : x_sf;
     a.h_sf_out = at<uint8_t>(workspace, L.h_sf);
-    if ((st = stage_mark(2, stream)) != MOEFP4_OK) return st;
-    st = hip_status(L.nt == 1   ? moefp4::launch_fc_decode(a, L.a4 ? 3 : 2, true, L.max_tiles, stream)
-                    : L.nt == 8 ? moefp4::launch_fc_gemm_a8(a, true, L.a4, p->w_layout == MOEFP4_W_GEMM,
-                                                            L.max_tiles, stream)
-                        : moefp4::launch_fc1_a8(a, L.max_tiles, stream),
-                    "fc1");
+  } else if (stage_f16) {
+    a.act = x;
+    a.act_scale = xs;
+    a.hmax_out = hmax;
+  } else if (L.g16_a16) {
+    uint16_t* x16 = at<uint16_t>(workspace, L.x16);
+    st = hip_status(moefp4::launch_rows_to_f16(static_cast<const uint16_t*>(x), p->T, p->H, x16, xs, stream),
+                    "rows_to_f16");
+    if (st != MOEFP4_OK) return st;
+    a.act = x16;
+    a.act_scale = xs;
+    a.hmax_out = hmax;
   } else {
-    if (stage_f16) {
-      a.act = x;
-      a.act_scale = xs;
-      a.hmax_out = hmax;
-    } else if (L.g16_a16) {
-      uint16_t* x16 = at<uint16_t>(workspace, L.x16);
-      st = hip_status(moefp4::launch_rows_to_f16(static_cast<const uint16_t*>(x), p->T, p->H, x16, xs,
-                                                 stream),
-                      "rows_to_f16");
-      if (st != MOEFP4_OK) return st;
-      a.act = x16;
-      a.act_scale = xs;
-      a.hmax_out = hmax;
-    } else {
-      a.act = x;
-    }
-    if ((st = stage_mark(2, stream)) != MOEFP4_OK) return st;
-    st = hip_status(L.nt == 1
-                        ? moefp4::launch_fc_decode(a, p->gran_k == 16 ? 0 : 1, true, L.max_tiles, stream)
-                        : moefp4::launch_fc1_a16(a, p->gran_k, L.max_tiles, stream),
-                    "fc1");
+    a.act = x;
   }
+  // FC2
+  moefp4::FcArgs b = a;
+  b.w = w2;
+  b.wsf = w2_sf;
+  b.gs = w2_gs;
+  b.K = p->I;
+  b.N = p->H;
+  b.act = at<void>(workspace, L.h);
+  b.act_sf = L.a8 ? at<uint8_t>(workspace, L.h_sf) : nullptr;
+  b.act_scale = nullptr;
+  b.hmax_in = hmax;
+  b.hmax_out = nullptr;
+  b.h_out = nullptr;
+  b.h_sf_out = nullptr;
+  b.y_out = at<float>(workspace, L.y);
+  const int mode = L.a4 ? 3 : L.a8 ? 2 : (p->gran_k == 16 ? 0 : 1);
+  if ((st = stage_mark(2, stream)) != MOEFP4_OK) return st;
+  st = hip_status(L.nt == 1   ? moefp4::launch_fc_decode(a, mode, true, L.max_tiles, stream)
+                  : L.nt == 8 ? moefp4::launch_fc_gemm_a8(a, true, L.a4, p->w_layout == MOEFP4_W_GEMM,
+                                                          L.max_tiles, stream)
+                  : L.a8      ? moefp4::launch_fc1_a8(a, L.max_tiles, stream)
+                              : moefp4::launch_fc1_a16(a, p->gran_k, L.max_tiles, stream),
+                  "fc1");
   if (st != MOEFP4_OK) return st;
   if ((st = stage_mark(3, stream)) != MOEFP4_OK) return st;
-
-  // FC2
-  a.w = w2;
-  a.wsf = w2_sf;
-  a.gs = w2_gs;
-  a.K = p->I;
-  a.N = p->H;
-  a.act = at<void>(workspace, L.h);
-  a.act_sf = L.a8 ? at<uint8_t>(workspace, L.h_sf) : nullptr;
-  a.act_scale = nullptr;
-  a.hmax_in = hmax;
-  a.hmax_out = nullptr;
-  a.h_out = nullptr;
-  a.h_sf_out = nullptr;
-  a.y_out = at<float>(workspace, L.y);
-  const int mode = L.a4 ? 3 : L.a8 ? 2 : (p->gran_k == 16 ? 0 : 1);
-  st = hip_status(L.nt == 1   ? moefp4::launch_fc_decode(a, mode, false, L.max_tiles, stream)
-                  : L.nt == 8 ? moefp4::launch_fc_gemm_a8(a, false, L.a4, p->w_layout == MOEFP4_W_GEMM,
+  st = hip_status(L.nt == 1   ? moefp4::launch_fc_decode(b, mode, false, L.max_tiles, stream)
+                  : L.nt == 8 ? moefp4::launch_fc_gemm_a8(b, false, L.a4, p->w_layout == MOEFP4_W_GEMM,
                                                           L.max_tiles, stream)
-                  : L.a8 ? moefp4::launch_fc2_a8(a, L.max_tiles, stream)
-                             : moefp4::launch_fc2_a16(a, p->gran_k, L.max_tiles, stream),
+                  : L.a8      ? moefp4::launch_fc2_a8(b, L.max_tiles, stream)
+                              : moefp4::launch_fc2_a16(b, p->gran_k, L.max_tiles, stream),
                   "fc2");
   if (st != MOEFP4_OK) return st;
   if ((st = stage_mark(4, stream)) != MOEFP4_OK) return st;
 
-  st = hip_status(moefp4::launch_combine(a.y_out, slot_of, topk_w, p->T, p->top_k, p->H, out,
+  st = hip_status(moefp4::launch_combine(b.y_out, slot_of, topk_w, p->T, p->top_k, p->H, out,
                                          p->out_fmt == MOEFP4_OUT_F32, stream),
                   "combine");
   if (st != MOEFP4_OK) return st;
@@ -537,6 +530,15 @@ moefp4_status moe_fp4_quantize_act_fp4(int64_t T, int64_t H, const void* x, uint
   moefp4_status st = hip_status(moefp4::launch_quantize_act(static_cast<const uint16_t*>(x), T, (int)H,
                                                             x_fp4, x_sf, true, stream),
                                 "quantize_act_fp4");
+  return st == MOEFP4_OK ? ok() : st;
+}
+
+moefp4_status moefp4_mfma_peak_probe(int32_t a4, int32_t iters, int32_t blocks, float* sink, double* flops,
+                                     hipStream_t stream) {
+  if (iters < 1 || blocks < 1 || !flops) return fail(MOEFP4_EINVAL, "iters, blocks >= 1 and flops non-NULL needed");
+  if (!sink) return fail(MOEFP4_EINVAL, "sink must be non-NULL (blocks * 256 floats)");
+  *flops = (double)blocks * 4 * (double)iters * 8 * 2.0 * 16 * 16 * 128;
+  moefp4_status st = hip_status(moefp4::launch_mfma_peak(a4 != 0, iters, blocks, sink, stream), "mfma_peak");
   return st == MOEFP4_OK ? ok() : st;
 }
 
