@@ -318,7 +318,7 @@ def measured_peaks(moe, torch):
         best = min(best, e0.elapsed_time(e1))
     copy_gbs = 2 * (1 << 30) / (best * 1e-3) / 1e9
     del a, b
-    blocks = 2048
+    blocks = torch.cuda.get_device_properties(0).multi_processor_count  # one workgroup per CU
     sink = torch.zeros(blocks * 256, dtype=torch.float32, device="cuda")
     res = {"copy_GBps": copy_gbs}
     for name, a4 in (("mfma_fp4xfp8_TFLOPs", False), ("mfma_fp4xfp4_TFLOPs", True)):
@@ -326,7 +326,7 @@ def measured_peaks(moe, torch):
         best, fl = 1e30, 0.0
         for _ in range(3):
             e0.record()
-            fl = moe.mfma_peak_probe(a4, 2000, blocks, sink)
+            fl = moe.mfma_peak_probe(a4, 4000, blocks, sink)
             e1.record()
             torch.cuda.synchronize()
             best = min(best, e0.elapsed_time(e1))

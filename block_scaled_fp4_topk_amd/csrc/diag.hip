@@ -9,25 +9,36 @@ namespace moefp4 {
 
 namespace {
 
-// 8 independent accumulator chains per wave (enough to keep the matrix pipe
-// busy); operands derived from the lane so the compiler cannot fold them.
+// 32 independent accumulator chains per wave (8 weight x 4 activation
+// operands, the shape of a GEMM stage), one workgroup of 4 waves per CU;
+// operands derived from the lane so the compiler cannot fold them.
 template <bool A4>
-__global__ __launch_bounds__(256) void mfma_peak_kernel(int iters, float* sink) {
+__global__ __launch_bounds__(256, 1) void mfma_peak_kernel(int iters, float* sink) {
   const int l = threadIdx.x;
-  const v8i a = {l, l * 3, l * 5, l * 7, 0, 0, 0, 0};
-  const v8i b = A4 ? v8i{l * 11, l * 13, l * 17, l * 19, 0, 0, 0, 0}
-                   : v8i{l * 11, l * 13, l * 17, l * 19, l * 23, l * 29, l * 31, l * 37};
-  v4f acc[8];
+  v4f acc[8][4];
 #pragma unroll
-  for (int c = 0; c < 8; ++c) acc[c] = v4f{0.f, 0.f, 0.f, 0.f};
-  for (int i = 0; i < iters; ++i) {
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
-      acc[c] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[c], 4, A4 ? 4 : 0, 0, 127, 0, 127);
+    for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  v8i w[8], x[4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w[i] = v8i{l + i, l * 3 + i, l ^ i, l + 7 * i, 0, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    x[i] = A4 ? v8i{l, i, l * 5, 3, 0, 0, 0, 0} : v8i{l, i, l * 5, 3, l + i, 9, l, i + 1};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int rg = 0; rg < 8; ++rg)
+#pragma unroll
+      for (int tg = 0; tg < 4; ++tg)
+        acc[rg][tg] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w[rg], x[tg], acc[rg][tg], 4, A4 ? 4 : 0, 0,
+                                                                      120 + rg, 0, 120 - tg);
   }
   float s = 0.f;
 #pragma unroll
-  for (int c = 0; c < 8; ++c) s += acc[c][0] + acc[c][1] + acc[c][2] + acc[c][3];
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s += acc[i][j][0] + acc[i][j][1] + acc[i][j][2] + acc[i][j][3];
   if (s == 1234.5f) sink[blockIdx.x * 256 + l] = s;  // never true for these operands; keeps the loop live
 }
 

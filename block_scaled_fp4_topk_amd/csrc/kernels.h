@@ -122,7 +122,7 @@ hipError_t launch_combine(const float* y, const int32_t* slot_of, const float* t
                           int k, int H, void* out, bool out_f32, hipStream_t s);
 
 // Register-only loop of the block-scaled MFMA (FP4 x FP8, or FP4 x FP4 with
-// a4): blocks x 4 waves x iters x 8 instructions of 2*16*16*128 flops.
+// a4): blocks x 4 waves x iters x 32 instructions of 2*16*16*128 flops.
 hipError_t launch_mfma_peak(bool a4, int iters, int blocks, float* sink, hipStream_t s);
 
 hipError_t launch_requant_g16_g32(const uint8_t* src, const uint8_t* src_sf, const float* gs,
