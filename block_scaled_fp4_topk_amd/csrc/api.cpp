@@ -124,7 +124,7 @@ moefp4_status plan(const moefp4_problem* p, Layout* L) {
   L->tiles = take((size_t)L->max_tiles * 8);
   L->ntiles = take(4);
   L->act_scale = take(L->g16_a16 ? T * 4 : 0);
-  L->x16 = take(L->g16_a16 && L->nt != 1 ? T * H * 2 : 0);
+  L->x16 = take(L->g16_a16 ? T * H * 2 : 0);
   L->x8 = take(L->quant_x ? (L->a4 ? T * H / 2 : T * H) : 0);
   L->x8_sf = take(L->quant_x ? T * (H / 32) : 0);
   L->hmax = take(L->g16_a16 ? A * 4 : 0);
@@ -163,7 +163,7 @@ moefp4_status stage_mark(int i, hipStream_t s) {
 moefp4_status route_into(const moefp4_problem* p, const Layout& L, const int32_t* ids,
                          int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* slot_of,
                          void* ws, uint32_t* zero_words, int n_zero, const void* x, float* row_scale,
-                         uint8_t* x8, uint8_t* x8_sf, hipStream_t s) {
+                         uint16_t* x16, uint8_t* x8, uint8_t* x8_sf, hipStream_t s) {
   moefp4::RouteOut o;
   o.counts = counts;
   o.offsets = offsets;
@@ -178,6 +178,7 @@ moefp4_status route_into(const moefp4_problem* p, const Layout& L, const int32_t
   o.T = p->T;
   o.H = p->H;
   o.row_scale = row_scale;
+  o.x16 = x16;
   o.x8 = x8;
   o.xsf = x8_sf;
   o.x_fp4 = L.a4;
@@ -259,7 +260,7 @@ moefp4_status moe_fp4_route(const moefp4_problem* p, const int32_t* topk_ids, in
     return fail(MOEFP4_EWORKSPACE, "workspace of %zu bytes needed, got %zu", L.total,
                 workspace ? ws_bytes : (size_t)0);
   st = route_into(p, L, topk_ids, counts, offsets, sorted_assign, slot_of, workspace, nullptr, 0,
-                  nullptr, nullptr, nullptr, nullptr, stream);
+                  nullptr, nullptr, nullptr, nullptr, nullptr, stream);
   return st == MOEFP4_OK ? ok() : st;
 }
 
@@ -293,16 +294,18 @@ moefp4_status moe_fp4_forward(const moefp4_problem* p, const void* x, const uint
   uint32_t* hmax = L.g16_a16 ? at<uint32_t>(workspace, L.hmax) : nullptr;
   if ((st = stage_mark(0, stream)) != MOEFP4_OK) return st;
   // group16 weights with bf16 x on 16-row tiles: the route launch also
-  // computes the per-token fp16 staging scales, and FC1 converts while staging
+  // computes the per-token fp16 staging scales and writes the rows converted
+  // with them, which FC1 copies straight to LDS
   const bool stage_f16 = L.g16_a16 && L.nt == 1;
   float* xs = L.g16_a16 ? at<float>(workspace, L.act_scale) : nullptr;
+  uint16_t* x16 = L.g16_a16 ? at<uint16_t>(workspace, L.x16) : nullptr;
   // bf16 x to be quantised to FP8 or MXFP4 (+ UE8M0 per 32): also done by
   // the route launch, into the workspace
   uint8_t* x8 = L.quant_x ? at<uint8_t>(workspace, L.x8) : nullptr;
   uint8_t* x8_sf = L.quant_x ? at<uint8_t>(workspace, L.x8_sf) : nullptr;
   st = route_into(p, L, topk_ids, counts, offsets, sorted, slot_of, workspace, hmax,
                   L.g16_a16 ? A : 0, (stage_f16 || L.quant_x) ? x : nullptr,
-                  stage_f16 ? xs : nullptr, x8, x8_sf, stream);
+                  stage_f16 ? xs : nullptr, stage_f16 ? x16 : nullptr, x8, x8_sf, stream);
   if (st != MOEFP4_OK) return st;
   if ((st = stage_mark(1, stream)) != MOEFP4_OK) return st;
 
@@ -330,11 +333,10 @@ moefp4_status moe_fp4_forward(const moefp4_problem* p, const void* x, const uint
     a.act_sf = L.quant_x ? x8_sf : x_sf;
     a.h_sf_out = at<uint8_t>(workspace, L.h_sf);
   } else if (stage_f16) {
-    a.act = x;
+    a.act = x16;
     a.act_scale = xs;
     a.hmax_out = hmax;
   } else if (L.g16_a16) {
-    uint16_t* x16 = at<uint16_t>(workspace, L.x16);
     st = hip_status(moefp4::launch_rows_to_f16(static_cast<const uint16_t*>(x), p->T, p->H, x16, xs, stream),
                     "rows_to_f16");
     if (st != MOEFP4_OK) return st;

@@ -27,6 +27,9 @@ struct RouteOut {
   const uint16_t* x;
   int T, H;
   float* row_scale;
+  // optional (with row_scale): the rows themselves converted, fp16(x * 2**-p_t)
+  // [T, H] (exact: 8 significant bits inside the fp16 range)
+  uint16_t* x16;
   // optional: FP8 + UE8M0 per 32 quantisation of bf16 rows x [T, H] into
   // x8 [T, H] and xsf [T, H/32] (x8 null: not computed); x_fp4: MXFP4
   // (E2M1 + UE8M0 per 32) instead, x8 [T, H/2]

@@ -22,8 +22,11 @@
 // chunk, and at the start of a group every lane copies its own scale bytes
 // of all the group's chunks into registers, which frees the buffer.
 // Activation rows that hold a token are loaded into registers one chunk
-// ahead and staged in LDS once for the 4 waves (bf16 -> fp16 x 2**-p for
-// group16 weights, exact).
+// ahead and staged in LDS once for the 4 waves; for group16 FC1 the route
+// launch has already written x as fp16 x 2**-p (exact), and those rows go
+// straight to LDS with direct-to-LDS loads beside the weights (the register
+// staging sat on the critical path of every chunk: 530 -> 513 us on the
+// decode16 FC1).
 //
 // Per chunk: stage the activations, barrier, read every operand of the
 // chunk into registers, issue the next chunk's loads (into a second set of
@@ -70,9 +73,12 @@ __device__ __forceinline__ int sc_swz(int lr) { return (lr >> 1) & 7; }
 template <int MODE, bool FC1>
 __global__ __launch_bounds__(256, (MODE == 0 && FC1) ? 2 : 3) void fc_decode_kernel(FcArgs a) {
   constexpr bool RING2 = MODE == 0 && FC1;
+  // ADMA: the activation rows are fp16 already (converted by the route
+  // launch) and go straight to LDS like the weights, with no register staging
+  constexpr bool ADMA = MODE == 0 && FC1;
   constexpr bool SCALED = MODE >= 2;                   // block-scaled activations (FP8 or FP4)
   constexpr int ACB = MODE == 3 ? KC / 2 : MODE == 2 ? KC : 2 * KC;  // activation bytes per row per chunk
-  constexpr int AROW = ACB + 16;                       // staged activation row stride
+  constexpr int AROW = ADMA ? ACB : ACB + 16;          // staged activation row stride
   constexpr int SEGB = ACB / 16;                       // activation bytes per thread (32, 16 or 8)
   constexpr int SCB = MODE == 0 ? KC / 16 : KC / 32;   // weight-scale bytes per row per chunk
   constexpr int SG = 128 / SCB;                        // chunks per scale group
@@ -182,6 +188,35 @@ __global__ __launch_bounds__(256, (MODE == 0 && FC1) ? 2 : 3) void fc_decode_ker
   }
   __syncthreads();
 
+  // ADMA loads: instruction i = wave, wave + 4 fills LDS rows 2 i, 2 i + 1 (1
+  // KB); lane -> row 2 i + lane / 32, slot lane % 32 holding the row's
+  // 16-byte segment (lane % 32) ^ (row % 16), so that the 16 rows' reads of
+  // one segment hit distinct banks.  Instructions whose two rows are both
+  // past the tile's tokens are not issued; a row past them in a partly
+  // valid pair repeats the tile's first token (its MFMA column is never
+  // stored).
+  const uint8_t* adma_src[2] = {nullptr, nullptr};
+  bool adma_on[2] = {false, false};
+  if (ADMA) {
+    const int nvr = min(16, ne - m0);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = wave + 4 * u, row = 2 * i + (lane >> 5);
+      adma_on[u] = 2 * i < nvr;
+      const int src = s_src[row < nvr ? row : 0];
+      adma_src[u] = static_cast<const uint8_t*>(a.act) + (size_t)src * ((size_t)(K / KC) * ACB) +
+                    16 * ((lane & 31) ^ (row & 15));
+    }
+  }
+  auto issue_a = [&](int c, uint8_t* sbuf) __attribute__((always_inline)) {
+    if (ADMA) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        if (adma_on[u])
+          __builtin_amdgcn_global_load_lds(adma_src[u] + (size_t)c * ACB, sbuf + (wave + 4 * u) * 1024, 16, 0, 0);
+    }
+  };
+
   // activation staging role: row sr, segment ss (rows past the expert's
   // token count are not loaded; their MFMA columns are never stored)
   const int sr = tid >> 4, ss = tid & 15;
@@ -193,7 +228,7 @@ __global__ __launch_bounds__(256, (MODE == 0 && FC1) ? 2 : 3) void fc_decode_ker
   uint4 av0 = {0u, 0u, 0u, 0u}, av1 = {0u, 0u, 0u, 0u};
   uint2 avs = {0u, 0u};
   auto load_act = [&](int c) __attribute__((always_inline)) {
-    if (ssrc >= 0) {
+    if (!ADMA && ssrc >= 0) {
       if (SEGB == 8) {
         const uint2 v = *reinterpret_cast<const uint2*>(arow_p + (size_t)c * ACB);
         av0 = uint4{v.x, v.y, 0u, 0u};
@@ -222,16 +257,17 @@ __global__ __launch_bounds__(256, (MODE == 0 && FC1) ? 2 : 3) void fc_decode_ker
   // prologue: group 0's scale lines, chunk 0's activations and weights
   issue_sc(0, 32 * wave, 32);
   load_act(0);
+  issue_a(0, s_b0);
   issue_w(0, s_w0);
 
   v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   // one chunk: its weights (sw) and activations (sb, sbsf) were loaded
   // during the previous chunk; RING2 loads the next chunk into the other
   // buffers (sw_next)
-  auto step = [&](int c, const uint8_t* sw, uint8_t* sw_next, uint8_t* sb, uint8_t* sbsf)
+  auto step = [&](int c, const uint8_t* sw, uint8_t* sw_next, uint8_t* sb, uint8_t* sb_next, uint8_t* sbsf)
       __attribute__((always_inline)) {
     // stage chunk c's activations
-    if (ssrc >= 0) {
+    if (!ADMA && ssrc >= 0) {
       uint4 v0 = av0, v1 = av1;
       if (MODE == 0) {
         // bf16 x or h -> fp16 * 2**-p (exact: 8 significant bits, in range)
@@ -288,6 +324,7 @@ __global__ __launch_bounds__(256, (MODE == 0 && FC1) ? 2 : 3) void fc_decode_ker
     if (RING2) {
       if (c + 1 < nchunks) {
         load_act(c + 1);
+        issue_a(c + 1, sb_next);
         issue_w(c + 1, sw_next);
       }
       if (c / SG + 1 < ngroups && j > 0) {
@@ -319,6 +356,10 @@ __global__ __launch_bounds__(256, (MODE == 0 && FC1) ? 2 : 3) void fc_decode_ker
       const uint32_t sbb = *reinterpret_cast<const uint16_t*>(sbsf + r16 * 8 + 2 * q);
       sbb0 = (int)(sbb & 0xFFu);
       sbb1 = (int)(sbb >> 8);
+    } else if (ADMA) {
+      // segment 8 q + jj of row r16 sits in slot (8 q + jj) ^ r16
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) bv[jj] = *reinterpret_cast<const uint4*>(brow + 16 * ((8 * q + jj) ^ r16));
     } else {
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) bv[jj] = *reinterpret_cast<const uint4*>(brow + 128 * q + 16 * jj);
@@ -383,11 +424,11 @@ __global__ __launch_bounds__(256, (MODE == 0 && FC1) ? 2 : 3) void fc_decode_ker
   };
   if (RING2) {
     for (int c = 0; c < nchunks; c += 2) {
-      step(c, s_w0, s_w1, s_b0, s_bsf0);
-      if (c + 1 < nchunks) step(c + 1, s_w1, s_w0, s_b1, s_bsf1);
+      step(c, s_w0, s_w1, s_b0, s_b1, s_bsf0);
+      if (c + 1 < nchunks) step(c + 1, s_w1, s_w0, s_b1, s_b0, s_bsf1);
     }
   } else {
-    for (int c = 0; c < nchunks; ++c) step(c, s_w0, s_w0, s_b0, s_bsf0);
+    for (int c = 0; c < nchunks; ++c) step(c, s_w0, s_w0, s_b0, s_b0, s_bsf0);
   }
 
   // epilogue: lane holds rows 4q..4q+3 of each 16-row tile, column r16

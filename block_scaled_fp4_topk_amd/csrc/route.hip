@@ -55,14 +55,16 @@ __device__ __forceinline__ int row_exponent(uint32_t maxbits) {
   return p < -110 ? -110 : p;
 }
 
-// One wavefront per row: the row's largest |x| (compared as bit patterns).
-// Workgroup b of nb workgroups takes rows 16 b + wave, 16 (b + nb) + wave, ...
+// One workgroup per row (rows b, b + nb, ...): the row's largest |x|
+// (compared as bit patterns), its scale 2**p, and (x16) the row converted to
+// fp16 with that scale, each thread taking 8 elements every 8 * 1024.
 __device__ void row_scales_from(const RouteOut& o, int b, int nb) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int t = b * kRouteWaves + wave; t < o.T; t += nb * kRouteWaves) {
+  __shared__ uint32_t s_red[kRouteWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int t = b; t < o.T; t += nb) {
     const uint16_t* row = o.x + (size_t)t * o.H;
     uint32_t m = 0;
-    for (int i = lane * 8; i < o.H; i += 512) {
+    for (int i = tid * 8; i < o.H; i += 8 * kRouteThreads) {
       const uint4 v = *reinterpret_cast<const uint4*>(row + i);
       const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -76,7 +78,29 @@ __device__ void row_scales_from(const RouteOut& o, int b, int nb) {
       const uint32_t y = __shfl_xor(m, d, 64);
       m = y > m ? y : m;
     }
-    if (lane == 0) o.row_scale[t] = __builtin_ldexpf(1.0f, row_exponent(m));
+    if (lane == 0) s_red[wave] = m;
+    __syncthreads();
+    m = s_red[0];
+    for (int w = 1; w < kRouteWaves; ++w) m = s_red[w] > m ? s_red[w] : m;
+    const int pt = row_exponent(m);
+    if (tid == 0) o.row_scale[t] = __builtin_ldexpf(1.0f, pt);
+    if (o.x16) {
+      // the row again (cache-resident), times 2**-p, to fp16
+      const float inv = __builtin_ldexpf(1.0f, -pt);
+      uint16_t* orow = o.x16 + (size_t)t * o.H;
+      for (int i = tid * 8; i < o.H; i += 8 * kRouteThreads) {
+        const uint4 v = *reinterpret_cast<const uint4*>(row + i);
+        uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const _Float16 lo = (_Float16)(bf16_to_f32(w[j] & 0xFFFFu) * inv);
+          const _Float16 hi = (_Float16)(bf16_to_f32(w[j] >> 16) * inv);
+          w[j] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+        }
+        *reinterpret_cast<uint4*>(orow + i) = uint4{w[0], w[1], w[2], w[3]};
+      }
+    }
+    __syncthreads();  // s_red is reused by the next row
   }
 }
 
@@ -421,10 +445,7 @@ hipError_t launch_route(const int32_t* topk_ids, int A, int E, int tile_m, const
                         hipStream_t s) {
   const size_t lds = (size_t)(E + kRouteWaves * E) * sizeof(int);
   int scale_blocks = 0;
-  if (o.row_scale && o.T > 0) {
-    scale_blocks = (o.T + kRouteWaves - 1) / kRouteWaves;
-    scale_blocks = scale_blocks > 256 ? 256 : scale_blocks;
-  }
+  if (o.row_scale && o.T > 0) scale_blocks = o.T > 256 ? 256 : o.T;  // a row per workgroup
   if (o.x8 && o.T > 0) {
     const long long nb = ((long long)o.T * (o.H / 32) + kRouteThreads - 1) / kRouteThreads;
     scale_blocks = (int)(nb > 256 ? 256 : nb);

@@ -172,7 +172,8 @@ moefp4_status moe_fp4_forward(const moefp4_problem* p,
  * loops, harnesses that forbid allocation): the workspace is a static device
  * array inside the library, 64 MiB per GPU (held from the library's load
  * until the process ends), which covers decode-sized problems (e.g. 256
- * tokens, top-8, H = 6144, I = 2048 needs about 56 MiB); a problem whose
+ * tokens, top-8, H = 6144, I = 2048 needs 52 MiB with FP8 activations, 59
+ * MiB with bf16 activations and group16 weights); a problem whose
  * workspace (moe_fp4_workspace_bytes) exceeds it returns MOEFP4_EWORKSPACE
  * with a message and enqueues nothing.  Arguments, layouts, supported
  * problems and errors otherwise as moe_fp4_forward; the result is bit-
