@@ -219,3 +219,30 @@ def test_many_items_per_workgroup():
     check_h(ws, p, hrows, "many items sampled")
     got = out[tokens][:, torch.from_numpy(cols).cuda()].cpu().numpy().astype(np.float64)
     check_bound(got, ref, "many items sampled", band)
+
+
+@pytest.mark.parametrize("gran,act", [(16, "bf16"), (32, "fp8")])
+def test_decode_largest_batch(gran, act):
+    """The largest decode-shaped batch: 8192 assignments over 512 experts
+    (16 per active expert, the most that still takes 16-row tiles, and the
+    most the single-workgroup route takes); for bf16 x on group16 weights the
+    route launch's 256 extra workgroups write the fp16 rows (4 each) that FC1
+    copies to LDS.  The oracle checks a sample of tokens spread over the
+    batch on every output column."""
+    require_gpu()
+    cfg = synth.variant(synth.CONFIGS["tiny"], name="decode_largest", T=1024, E=512, k=8, H=512, I=256,
+                        gran=gran, act=act, global_scale="uniform" if gran == 16 else "none", seed=43)
+    inp = synth.make_moe_inputs(cfg)
+    counts = np.bincount(inp.topk_ids.ravel(), minlength=cfg.E)
+    assert cfg.T * cfg.k == 8192 and cfg.T * cfg.k / np.count_nonzero(counts) <= 16
+    d = to_dev(inp)
+    print(f"decode largest batch {act}-g{gran}: T={cfg.T} E={cfg.E} k={cfg.k}, "
+          f"{np.count_nonzero(counts)} active experts, up to {counts.max()} rows: running on GPU", flush=True)
+    out, ws, p = forward_ws(inp, d)
+    torch.cuda.synchronize()
+    tokens = sorted({0, 1, 3, 4, 255, 256, cfg.T // 2, cfg.T - 2, cfg.T - 1}
+                    | set(np.random.default_rng(7).choice(cfg.T, size=23, replace=False).tolist()))
+    ref, band, hrows = ref_forward(inp, tokens=tokens, return_h=True)
+    check_h(ws, p, hrows, f"decode largest batch {act}-g{gran}")
+    got = out[tokens].cpu().numpy().astype(np.float64)
+    check_bound(got, ref, f"decode largest batch {act}-g{gran}", band)
