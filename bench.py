@@ -37,6 +37,9 @@ WORKLOAD_TEXT = {
     "decode32": "FP8xFP4 decode: T=256 E=256 top-8 H=6144 I=2048, E4M3+UE8M0 k32 x, E2M1 + UE8M0 k32",
     "decode32_a4": "A4 decode: T=256 E=256 top-8 H=6144 I=2048, bf16 x quantised by the library to MXFP4 "
                    "(E2M1+UE8M0 k32), h MXFP4, E2M1 + UE8M0 k32 weights",
+    "decode16_fused": "W4A16 NVFP4 decode as decode16, FC1 and FC2 in one persistent launch "
+                      "(moe_fp4_forward_fused)",
+    "decode32_fused": "FP8xFP4 decode as decode32, FC1 and FC2 in one persistent launch (moe_fp4_forward_fused)",
     "prefill32": "prefill: T=8192 E=256 top-8 Zipf(1.1) H=6144 I=2048, E4M3+UE8M0 k32 x, E2M1 + UE8M0 k32",
     "prefill32_bf16q": "prefill: T=8192 E=256 top-8 Zipf(1.1) H=6144 I=2048, bf16 x quantised by the "
                        "library to E4M3+UE8M0 k32, E2M1 + UE8M0 k32",
@@ -123,7 +126,8 @@ def gpu_forward_into(moe, torch, inp, d, ws, out):
     moe.forward(d["x"], d["topk_ids"], d["topk_w"], d["w13"], d["w13_sf"], d["w13_gs"], d["w2"],
                 d["w2_sf"], d["w2_gs"], inp.cfg.gran, x_sf=d["x_sf"], out=out, workspace=ws,
                 quantize_x={"bf16q": "fp8", "bf16q4": "fp4"}.get(inp.cfg.act, False),
-                w_layout="gemm" if inp.cfg.name.endswith("_prep") else "raw")
+                w_layout="gemm" if inp.cfg.name.endswith("_prep") else "raw",
+                fused=inp.cfg.name.endswith("_fused"))
 
 
 def stage_kernel(cfg, ids, stage):
@@ -153,7 +157,7 @@ def workload_cfg(synth, name):
     if name in synth.CONFIGS:
         return synth.CONFIGS[name]
     base, _, form = name.partition("_")
-    if form == "prep":
+    if form in ("prep", "fused"):
         return synth.variant(synth.CONFIGS[base], name=name)
     return synth.variant(synth.CONFIGS[base], name=name,
                          act="bf16q4" if form in ("a4", "a4_prep") else "bf16q")
@@ -517,8 +521,8 @@ def secondary(moe, torch, synth, args, inp16, d16, peaks):
     del d16
     torch.cuda.empty_cache()
     out["requant_layer"] = requant_layer(moe, torch, inp16)
-    for name in ("decode32", "decode32_a4", "prefill32", "prefill32_bf16q", "prefill32_a4", "prefill32_prep",
-                 "prefill32_a4_prep"):
+    for name in ("decode32", "decode32_a4", "decode16_fused", "decode32_fused", "prefill32", "prefill32_bf16q",
+                 "prefill32_a4", "prefill32_prep", "prefill32_a4_prep"):
         cfg = workload_cfg(synth, name)
         print(f"[bench] secondary {name}", file=sys.stderr, flush=True)
         inp = synth.make_moe_inputs(cfg)

@@ -10,7 +10,7 @@ Functions mirror the C entry points:
   workspace_bytes(problem)            -> moe_fp4_workspace_bytes
   workspace_offsets(problem)          -> moe_fp4_workspace_offsets
   route(problem, topk_ids, ...)       -> moe_fp4_route
-  forward(x, topk_ids, topk_w, ...)   -> moe_fp4_forward
+  forward(x, topk_ids, topk_w, ...)   -> moe_fp4_forward (fused=True: moe_fp4_forward_fused)
   forward_static(x, topk_ids, ...)    -> moe_fp4_forward_static (no workspace)
   requant_gran_k(src, src_sf, ...)    -> fp4_requant_gran_k
   prepare_gemm_weights(src, src_sf, ...) -> moe_fp4_prepare_gemm_weights
@@ -73,6 +73,8 @@ def lib():
         L.moe_fp4_forward.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                       _P, _P, ctypes.c_size_t, _P]
         L.moe_fp4_forward.restype = st
+        L.moe_fp4_forward_fused.argtypes = L.moe_fp4_forward.argtypes
+        L.moe_fp4_forward_fused.restype = st
         L.moe_fp4_forward_static.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                              _P, _P]
         L.moe_fp4_forward_static.restype = st
@@ -214,15 +216,16 @@ def forward_problem(x, topk_ids, w13, w2, gran_k, x_sf=None, w13_order="gate_up"
 
 def forward(x, topk_ids, topk_w, w13, w13_sf, w13_gs, w2, w2_sf, w2_gs, gran_k, x_sf=None,
             w13_order="gate_up", out=None, workspace=None, stream=None, out_dtype=None,
-            quantize_x=False, w_layout="raw"):
+            quantize_x=False, w_layout="raw", fused=False):
     """MoE forward on the GPU.  x: [T, H] bfloat16 (A16); uint8/float8_e4m3fn
     [T, H] with x_sf [T, H/32] uint8 (A8); or uint8 [T, H/2] (two E2M1 codes
     per byte) with x_sf (A4).  quantize_x with bfloat16 x asks the library to
     quantise x first: True or "fp8" -> the A8 format (act_fmt
     BF16_QUANT_FP8_K32), "fp4" -> the A4 format (BF16_QUANT_FP4_K32).
     Weights uint8 as in include/moefp4.h; w_layout="gemm" for weights from
-    prepare_gemm_weights.  Returns out [T, H] bfloat16 (default) or float32
-    (out_dtype=torch.float32)."""
+    prepare_gemm_weights.  fused=True runs FC1 and FC2 in one persistent
+    launch (moe_fp4_forward_fused; 16-row decode tiles only, same result).
+    Returns out [T, H] bfloat16 (default) or float32 (out_dtype=torch.float32)."""
     import torch
     u8 = (torch.uint8,)
     fp8 = (torch.uint8, torch.float8_e4m3fn)
@@ -242,9 +245,10 @@ def forward(x, topk_ids, topk_w, w13, w13_sf, w13_gs, w2, w2_sf, w2_gs, gran_k, 
         out = torch.empty((p.T, p.H), dtype=out_dtype, device=x.device)
     _dev(out, "out", (out_dtype,))
     ws = _workspace(p, workspace, x.device)
-    _check(lib().moe_fp4_forward(ctypes.byref(p), _ptr(x), _ptr(x_sf), _ptr(topk_ids), _ptr(topk_w),
-                                 _ptr(w13), _ptr(w13_sf), _ptr(w13_gs), _ptr(w2), _ptr(w2_sf),
-                                 _ptr(w2_gs), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
+    fn = lib().moe_fp4_forward_fused if fused else lib().moe_fp4_forward
+    _check(fn(ctypes.byref(p), _ptr(x), _ptr(x_sf), _ptr(topk_ids), _ptr(topk_w), _ptr(w13), _ptr(w13_sf),
+              _ptr(w13_gs), _ptr(w2), _ptr(w2_sf), _ptr(w2_gs), _ptr(out), _ptr(ws), ws.numel(),
+              _stream(stream)))
     return out
 
 

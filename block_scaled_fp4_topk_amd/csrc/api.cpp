@@ -39,7 +39,8 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
   size_t flags, counts, offsets, sorted, slot_of, tiles, ntiles;
-  size_t act_scale, x16, x8, x8_sf, hmax, h, h_sf, y, route_hist, total;
+  size_t act_scale, x16, x8, x8_sf, sync, hmax, h, h_sf, y, route_hist, total;
+  int sync_words, zero_words;  // decode: queue + done counters; + hmax words (all cleared by the route launch)
   int route_chunks, route_chunk;
   int tile_m, nt, max_tiles;
   bool a8, a4, quant_x, g16_a16;
@@ -127,7 +128,12 @@ moefp4_status plan(const moefp4_problem* p, Layout* L) {
   L->x16 = take(L->g16_a16 ? T * H * 2 : 0);
   L->x8 = take(L->quant_x ? (L->a4 ? T * H / 2 : T * H) : 0);
   L->x8_sf = take(L->quant_x ? T * (H / 32) : 0);
-  L->hmax = take(L->g16_a16 ? A * 4 : 0);
+  // the single-launch decode kernel's counters, then the per-slot h maxima
+  // (group16 with bf16 x): one region the route launch clears
+  L->sync_words = L->nt == 1 ? moefp4::decode_sync_words(L->max_tiles) : 0;
+  L->zero_words = L->sync_words + (L->g16_a16 ? (int)A : 0);
+  L->sync = take((size_t)L->zero_words * 4);
+  L->hmax = L->sync + (size_t)L->sync_words * 4;
   L->h = take(L->a4 ? A * I / 2 : L->a8 ? A * I : A * I * 2);
   L->h_sf = take(L->a8 ? A * (I / 32) : 0);
   L->y = take(A * H * 4);
@@ -225,53 +231,16 @@ moefp4_status static_scratch(void** ptr) {
 
 }  // namespace
 
-extern "C" {
+namespace {
 
-moefp4_status moe_fp4_workspace_bytes(const moefp4_problem* p, size_t* bytes) {
-  if (!bytes) return fail(MOEFP4_EINVAL, "bytes is NULL");
-  Layout L;
-  moefp4_status st = plan(p, &L);
-  if (st != MOEFP4_OK) return st;
-  *bytes = L.total;
-  return ok();
-}
-
-moefp4_status moe_fp4_workspace_offsets(const moefp4_problem* p, size_t* h, size_t* h_sf, size_t* slot_of) {
-  if (!h || !h_sf || !slot_of) return fail(MOEFP4_EINVAL, "h, h_sf and slot_of must be non-NULL");
-  Layout L;
-  moefp4_status st = plan(p, &L);
-  if (st != MOEFP4_OK) return st;
-  *h = L.h;
-  *h_sf = L.a8 ? L.h_sf : 0;
-  *slot_of = L.slot_of;
-  return ok();
-}
-
-moefp4_status moe_fp4_route(const moefp4_problem* p, const int32_t* topk_ids, int32_t* counts,
-                            int32_t* offsets, int32_t* sorted_assign, int32_t* slot_of,
-                            void* workspace, size_t ws_bytes, hipStream_t stream) {
-  Layout L;
-  moefp4_status st = plan(p, &L);
-  if (st != MOEFP4_OK) return st;
-  if (p->T > 0 && (!topk_ids || !sorted_assign || !slot_of))
-    return fail(MOEFP4_EINVAL, "topk_ids, sorted_assign and slot_of must be non-NULL");
-  if (!counts || !offsets) return fail(MOEFP4_EINVAL, "counts and offsets must be non-NULL");
-  if (!workspace || ws_bytes < L.total)
-    return fail(MOEFP4_EWORKSPACE, "workspace of %zu bytes needed, got %zu", L.total,
-                workspace ? ws_bytes : (size_t)0);
-  st = route_into(p, L, topk_ids, counts, offsets, sorted_assign, slot_of, workspace, nullptr, 0,
-                  nullptr, nullptr, nullptr, nullptr, nullptr, stream);
-  return st == MOEFP4_OK ? ok() : st;
-}
-
-moefp4_status moe_fp4_forward(const moefp4_problem* p, const void* x, const uint8_t* x_sf,
-                              const int32_t* topk_ids, const float* topk_w, const uint8_t* w13,
-                              const uint8_t* w13_sf, const float* w13_gs, const uint8_t* w2,
-                              const uint8_t* w2_sf, const float* w2_gs, void* out,
-                              void* workspace, size_t ws_bytes, hipStream_t stream) {
-  Layout L;
-  moefp4_status st = plan(p, &L);
-  if (st != MOEFP4_OK) return st;
+// The forward; fused: FC1 and FC2 in one persistent launch (16-row decode
+// tiles only, checked by the caller).
+moefp4_status forward_impl(const moefp4_problem* p, const Layout& L, const void* x, const uint8_t* x_sf,
+                           const int32_t* topk_ids, const float* topk_w, const uint8_t* w13,
+                           const uint8_t* w13_sf, const float* w13_gs, const uint8_t* w2,
+                           const uint8_t* w2_sf, const float* w2_gs, void* out, void* workspace,
+                           size_t ws_bytes, bool fused, hipStream_t stream) {
+  moefp4_status st = MOEFP4_OK;
   if (p->T == 0) return ok();
   if (!x || !topk_ids || !topk_w || !w13 || !w13_sf || !w2 || !w2_sf || !out)
     return fail(MOEFP4_EINVAL, "x, topk_ids, topk_w, w13, w13_sf, w2, w2_sf and out must be non-NULL");
@@ -292,6 +261,7 @@ moefp4_status moe_fp4_forward(const moefp4_problem* p, const void* x, const uint
   int32_t* sorted = at<int32_t>(workspace, L.sorted);
   int32_t* slot_of = at<int32_t>(workspace, L.slot_of);
   uint32_t* hmax = L.g16_a16 ? at<uint32_t>(workspace, L.hmax) : nullptr;
+  uint32_t* zero = L.zero_words ? at<uint32_t>(workspace, L.sync) : nullptr;
   if ((st = stage_mark(0, stream)) != MOEFP4_OK) return st;
   // group16 weights with bf16 x on 16-row tiles: the route launch also
   // computes the per-token fp16 staging scales and writes the rows converted
@@ -303,8 +273,8 @@ moefp4_status moe_fp4_forward(const moefp4_problem* p, const void* x, const uint
   // the route launch, into the workspace
   uint8_t* x8 = L.quant_x ? at<uint8_t>(workspace, L.x8) : nullptr;
   uint8_t* x8_sf = L.quant_x ? at<uint8_t>(workspace, L.x8_sf) : nullptr;
-  st = route_into(p, L, topk_ids, counts, offsets, sorted, slot_of, workspace, hmax,
-                  L.g16_a16 ? A : 0, (stage_f16 || L.quant_x) ? x : nullptr,
+  st = route_into(p, L, topk_ids, counts, offsets, sorted, slot_of, workspace, zero,
+                  L.zero_words, (stage_f16 || L.quant_x) ? x : nullptr,
                   stage_f16 ? xs : nullptr, stage_f16 ? x16 : nullptr, x8, x8_sf, stream);
   if (st != MOEFP4_OK) return st;
   if ((st = stage_mark(1, stream)) != MOEFP4_OK) return st;
@@ -363,21 +333,35 @@ moefp4_status moe_fp4_forward(const moefp4_problem* p, const void* x, const uint
   b.y_out = at<float>(workspace, L.y);
   const int mode = L.a4 ? 3 : L.a8 ? 2 : (p->gran_k == 16 ? 0 : 1);
   if ((st = stage_mark(2, stream)) != MOEFP4_OK) return st;
-  st = hip_status(L.nt == 1   ? moefp4::launch_fc_decode(a, mode, true, L.max_tiles, stream)
-                  : L.nt == 8 ? moefp4::launch_fc_gemm_a8(a, true, L.a4, p->w_layout == MOEFP4_W_GEMM,
-                                                          L.max_tiles, stream)
-                  : L.a8      ? moefp4::launch_fc1_a8(a, L.max_tiles, stream)
-                              : moefp4::launch_fc1_a16(a, p->gran_k, L.max_tiles, stream),
-                  "fc1");
-  if (st != MOEFP4_OK) return st;
-  if ((st = stage_mark(3, stream)) != MOEFP4_OK) return st;
-  st = hip_status(L.nt == 1   ? moefp4::launch_fc_decode(b, mode, false, L.max_tiles, stream)
-                  : L.nt == 8 ? moefp4::launch_fc_gemm_a8(b, false, L.a4, p->w_layout == MOEFP4_W_GEMM,
-                                                          L.max_tiles, stream)
-                  : L.a8      ? moefp4::launch_fc2_a8(b, L.max_tiles, stream)
-                              : moefp4::launch_fc2_a16(b, p->gran_k, L.max_tiles, stream),
-                  "fc2");
-  if (st != MOEFP4_OK) return st;
+  if (fused) {
+    // FC1 and FC2 in one persistent launch (16-row decode tiles)
+    moefp4::DecodeSync y;
+    y.queue = at<int32_t>(workspace, L.sync);
+    y.done = y.queue + 8;
+    y.err = at<int32_t>(workspace, L.flags) + 1;
+    y.nx = moefp4::xcd_count();
+    y.nblk1 = p->I / 64;
+    y.nblk2 = p->H / 128;
+    st = hip_status(moefp4::launch_fc_decode_fused(a, b, mode, y, stream), "fc1+fc2");
+    if (st != MOEFP4_OK) return st;
+    if ((st = stage_mark(3, stream)) != MOEFP4_OK) return st;
+  } else {
+    st = hip_status(L.nt == 1   ? moefp4::launch_fc_decode(a, mode, true, L.max_tiles, stream)
+                    : L.nt == 8 ? moefp4::launch_fc_gemm_a8(a, true, L.a4, p->w_layout == MOEFP4_W_GEMM,
+                                                            L.max_tiles, stream)
+                    : L.a8      ? moefp4::launch_fc1_a8(a, L.max_tiles, stream)
+                                : moefp4::launch_fc1_a16(a, p->gran_k, L.max_tiles, stream),
+                    "fc1");
+    if (st != MOEFP4_OK) return st;
+    if ((st = stage_mark(3, stream)) != MOEFP4_OK) return st;
+    st = hip_status(L.nt == 1   ? moefp4::launch_fc_decode(b, mode, false, L.max_tiles, stream)
+                    : L.nt == 8 ? moefp4::launch_fc_gemm_a8(b, false, L.a4, p->w_layout == MOEFP4_W_GEMM,
+                                                            L.max_tiles, stream)
+                    : L.a8      ? moefp4::launch_fc2_a8(b, L.max_tiles, stream)
+                                : moefp4::launch_fc2_a16(b, p->gran_k, L.max_tiles, stream),
+                    "fc2");
+    if (st != MOEFP4_OK) return st;
+  }
   if ((st = stage_mark(4, stream)) != MOEFP4_OK) return st;
 
   st = hip_status(moefp4::launch_combine(b.y_out, slot_of, topk_w, p->T, p->top_k, p->H, out,
@@ -386,6 +370,76 @@ moefp4_status moe_fp4_forward(const moefp4_problem* p, const void* x, const uint
   if (st != MOEFP4_OK) return st;
   if ((st = stage_mark(5, stream)) != MOEFP4_OK) return st;
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+moefp4_status moe_fp4_workspace_bytes(const moefp4_problem* p, size_t* bytes) {
+  if (!bytes) return fail(MOEFP4_EINVAL, "bytes is NULL");
+  Layout L;
+  moefp4_status st = plan(p, &L);
+  if (st != MOEFP4_OK) return st;
+  *bytes = L.total;
+  return ok();
+}
+
+moefp4_status moe_fp4_workspace_offsets(const moefp4_problem* p, size_t* h, size_t* h_sf, size_t* slot_of) {
+  if (!h || !h_sf || !slot_of) return fail(MOEFP4_EINVAL, "h, h_sf and slot_of must be non-NULL");
+  Layout L;
+  moefp4_status st = plan(p, &L);
+  if (st != MOEFP4_OK) return st;
+  *h = L.h;
+  *h_sf = L.a8 ? L.h_sf : 0;
+  *slot_of = L.slot_of;
+  return ok();
+}
+
+moefp4_status moe_fp4_route(const moefp4_problem* p, const int32_t* topk_ids, int32_t* counts,
+                            int32_t* offsets, int32_t* sorted_assign, int32_t* slot_of,
+                            void* workspace, size_t ws_bytes, hipStream_t stream) {
+  Layout L;
+  moefp4_status st = plan(p, &L);
+  if (st != MOEFP4_OK) return st;
+  if (p->T > 0 && (!topk_ids || !sorted_assign || !slot_of))
+    return fail(MOEFP4_EINVAL, "topk_ids, sorted_assign and slot_of must be non-NULL");
+  if (!counts || !offsets) return fail(MOEFP4_EINVAL, "counts and offsets must be non-NULL");
+  if (!workspace || ws_bytes < L.total)
+    return fail(MOEFP4_EWORKSPACE, "workspace of %zu bytes needed, got %zu", L.total,
+                workspace ? ws_bytes : (size_t)0);
+  st = route_into(p, L, topk_ids, counts, offsets, sorted_assign, slot_of, workspace, nullptr, 0,
+                  nullptr, nullptr, nullptr, nullptr, nullptr, stream);
+  return st == MOEFP4_OK ? ok() : st;
+}
+
+moefp4_status moe_fp4_forward(const moefp4_problem* p, const void* x, const uint8_t* x_sf,
+                              const int32_t* topk_ids, const float* topk_w, const uint8_t* w13,
+                              const uint8_t* w13_sf, const float* w13_gs, const uint8_t* w2,
+                              const uint8_t* w2_sf, const float* w2_gs, void* out,
+                              void* workspace, size_t ws_bytes, hipStream_t stream) {
+  Layout L;
+  moefp4_status st = plan(p, &L);
+  if (st != MOEFP4_OK) return st;
+  return forward_impl(p, L, x, x_sf, topk_ids, topk_w, w13, w13_sf, w13_gs, w2, w2_sf, w2_gs, out, workspace,
+                      ws_bytes, false, stream);
+}
+
+moefp4_status moe_fp4_forward_fused(const moefp4_problem* p, const void* x, const uint8_t* x_sf,
+                                    const int32_t* topk_ids, const float* topk_w, const uint8_t* w13,
+                                    const uint8_t* w13_sf, const float* w13_gs, const uint8_t* w2,
+                                    const uint8_t* w2_sf, const float* w2_gs, void* out, void* workspace,
+                                    size_t ws_bytes, hipStream_t stream) {
+  Layout L;
+  moefp4_status st = plan(p, &L);
+  if (st != MOEFP4_OK) return st;
+  if (L.nt != 1)
+    return fail(MOEFP4_EUNSUPPORTED,
+                "the single-launch forward runs the 16-row decode tiles only (at most 16 assignments per active "
+                "expert); this problem runs on the %s tiles: use moe_fp4_forward",
+                L.nt == 8 ? "128-row GEMM" : "64-row");
+  return forward_impl(p, L, x, x_sf, topk_ids, topk_w, w13, w13_sf, w13_gs, w2, w2_sf, w2_gs, out, workspace,
+                      ws_bytes, true, stream);
 }
 
 moefp4_status moe_fp4_forward_static(const moefp4_problem* p, const void* x, const uint8_t* x_sf,

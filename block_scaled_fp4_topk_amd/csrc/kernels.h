@@ -99,6 +99,30 @@ hipError_t launch_fc2_a8(const FcArgs& a, int max_tiles, hipStream_t s);
 // I % 64 == 0 (FC1) and H % 128 == 0 (FC2).
 hipError_t launch_fc_decode(const FcArgs& a, int mode, bool fc1, int max_tiles, hipStream_t s);
 
+// Single-launch decode (FC1 + SwiGLU + h quantisation, then FC2) in one
+// persistent kernel.  Each expert tile's FC1 and FC2 items run on one XCD
+// (tile t on XCD t % nx), taken from that XCD's queue in order (every FC1
+// item before any FC2 item), so h passes from FC1 to FC2 through the XCD's
+// own L2: an FC1 item waits for its stores and bumps done[t]; an FC2 item
+// waits until done[t] counts every FC1 row block of its tile, then drops its
+// CU's L1 lines.  queue [nx] and done [max_tiles] are zeroed by the route
+// launch (which also clears *err); err counts waits that exceeded their
+// time limit (the kernel then finishes with wrong results instead of
+// hanging).
+struct DecodeSync {
+  int32_t* queue;
+  int32_t* done;
+  int32_t* err;
+  int nx;            // XCDs (workgroups read their XCD id from the hardware)
+  int nblk1, nblk2;  // FC1 / FC2 row blocks per tile
+};
+hipError_t launch_fc_decode_fused(const FcArgs& a1, const FcArgs& a2, int mode, const DecodeSync& y,
+                                  hipStream_t s);
+// words of the DecodeSync queue + done counters for max_tiles tiles
+inline int decode_sync_words(int max_tiles) { return 8 + max_tiles; }
+// XCDs of the current device (32 CUs each on MI355X), 1..8
+int xcd_count();
+
 // Prefill-shaped FP8 x FP4 grouped GEMMs on 128-row expert tiles (direct-
 // to-LDS pipelined, 512 weight rows per work item); a4: MXFP4 activations
 // (act [rows, K/2], h written as MXFP4).  Needs H % 512 == 0, I % 512 == 0

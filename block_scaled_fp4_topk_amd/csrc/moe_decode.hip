@@ -63,15 +63,17 @@ __device__ __forceinline__ uint32_t dw(const uint4& v, int r) {
 // consecutive rows hit 16 distinct bank groups
 __device__ __forceinline__ int sc_swz(int lr) { return (lr >> 1) & 7; }
 
-// RING2: chunk buffers in pairs, so the next chunk's loads are issued right
-// after the chunk's barrier (two workgroups per CU, one barrier per chunk);
-// otherwise one set of buffers, refilled after a second barrier once every
-// wave has read its operands (three workgroups per CU).  Measured per kernel
-// on the decode16 geometry: the pair wins only where the MFMA phase is
-// longest (group16 FC1, 512 vs 545 us); elsewhere the extra workgroup per
-// CU wins (e.g. group16 FC2 268 vs 277 us, FP8 FC1 471 vs 486 us).
+// One item: expert tile `tile` (<= 16 activation rows of one expert) x weight
+// row block `rb` (FC1: gate rows [64 rb, 64 rb + 64) and the matching up
+// rows; FC2: output rows [128 rb, 128 rb + 128)), the whole K.  The LDS
+// arrays are the calling kernel's own __shared__ arrays, passed in (distinct
+// objects, so the compiler keeps the loads into one buffer apart from the
+// reads of another).
 template <int MODE, bool FC1>
-__global__ __launch_bounds__(256, (MODE == 0 && FC1) ? 2 : 3) void fc_decode_kernel(FcArgs a) {
+__device__ __forceinline__ void decode_item(const FcArgs& a, const int tile, const int rb, uint8_t* s_w0,
+                                            uint8_t* s_w1, uint8_t* s_sc, uint8_t* s_b0, uint8_t* s_b1,
+                                            uint8_t* s_bsf0, uint8_t* s_bsf1, int* s_src, float* s_rs,
+                                            float (*s_amax)[16]) {
   constexpr bool RING2 = MODE == 0 && FC1;
   // ADMA: the activation rows are fp16 already (converted by the route
   // launch) and go straight to LDS like the weights, with no register staging
@@ -83,22 +85,7 @@ __global__ __launch_bounds__(256, (MODE == 0 && FC1) ? 2 : 3) void fc_decode_ker
   constexpr int SCB = MODE == 0 ? KC / 16 : KC / 32;   // weight-scale bytes per row per chunk
   constexpr int SG = 128 / SCB;                        // chunks per scale group
   constexpr int RPC = WR / SG;                         // scale lines staged per chunk (16 or 8)
-  // RING2 pairs (even / odd chunks) are distinct arrays, so the loads into
-  // one never make the compiler wait before reading the other
-  constexpr int NB1 = RING2 ? 1 : 0;
-  __shared__ __attribute__((aligned(16))) uint8_t s_w0[WR * 128];
-  __shared__ __attribute__((aligned(16))) uint8_t s_w1[NB1 * WR * 128 + 16];
-  __shared__ __attribute__((aligned(16))) uint8_t s_sc[WR * 128];
-  __shared__ __attribute__((aligned(16))) uint8_t s_b0[16 * AROW];
-  __shared__ __attribute__((aligned(16))) uint8_t s_b1[NB1 * 16 * AROW + 16];
-  __shared__ __attribute__((aligned(16))) uint8_t s_bsf0[16 * 8];
-  __shared__ __attribute__((aligned(16))) uint8_t s_bsf1[NB1 * 16 * 8 + 16];
-  __shared__ int s_src[16];
-  __shared__ float s_rs[16];
-  __shared__ float s_amax[4][16];
 
-  const int tile = blockIdx.y;
-  if (tile >= a.ntiles[0]) return;
   const int e = a.tiles[2 * tile], m0 = a.tiles[2 * tile + 1];
   const int ne = a.counts[e], oe = a.offsets[e];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -115,10 +102,10 @@ __global__ __launch_bounds__(256, (MODE == 0 && FC1) ? 2 : 3) void fc_decode_ker
   // workgroup-local weight row (0..127) -> row of the expert's matrix
   auto wrow = [&](int lr) __attribute__((always_inline)) -> int {
     if (FC1) {
-      const int i0 = blockIdx.x * 64 + (lr & 63);
+      const int i0 = rb * 64 + (lr & 63);
       return ((lr >= 64) != (a.w13_order != 0)) ? a.I + i0 : i0;
     }
-    return blockIdx.x * 128 + lr;
+    return rb * 128 + lr;
   };
 
   // weight loads: instruction i of a wave covers rows 32 wave + 8 i .. + 8;
@@ -178,7 +165,9 @@ __global__ __launch_bounds__(256, (MODE == 0 && FC1) ? 2 : 3) void fc_decode_ker
         if (FC1) {
           sc = a.act_scale[src];
         } else {
-          const uint32_t hm = a.hmax_in[slot];
+          // (an atomic load: FC1 publishes the maxima with atomics, in the
+          // single-launch form during this same launch)
+          const uint32_t hm = __hip_atomic_load(a.hmax_in + slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           sc = __builtin_ldexpf(1.0f, hm ? (int)(hm >> 23) - 127 - 14 : 0);
         }
       }
@@ -243,7 +232,7 @@ __global__ __launch_bounds__(256, (MODE == 0 && FC1) ? 2 : 3) void fc_decode_ker
   // this lane's weight rows (workgroup-local)
   const int lrow0 = FC1 ? wave * 16 + r16 : wave * 32 + r16;
   const int lrow1 = FC1 ? 64 + wave * 16 + r16 : wave * 32 + 16 + r16;
-  int obase = FC1 ? blockIdx.x * 64 + wave * 16 : blockIdx.x * 128 + wave * 32;
+  int obase = FC1 ? rb * 64 + wave * 16 : rb * 128 + wave * 32;
 
   // the lane's weight-scale bytes of the current group, one entry per chunk
   // (group16: the 4 scales of K [64 q, 64 q + 64) for each of the two rows;
@@ -499,6 +488,143 @@ __global__ __launch_bounds__(256, (MODE == 0 && FC1) ? 2 : 3) void fc_decode_ker
   }
 }
 
+// The LDS arrays of an item (AROWV: the staged activation row stride the
+// items use; RING: the paired buffers).
+#define DECODE_LDS(AROWV, RING)                                                   \
+  constexpr int NB1_ = (RING) ? 1 : 0;                                            \
+  __shared__ __attribute__((aligned(16))) uint8_t s_w0[WR * 128];                 \
+  __shared__ __attribute__((aligned(16))) uint8_t s_w1[NB1_ * WR * 128 + 16];     \
+  __shared__ __attribute__((aligned(16))) uint8_t s_sc[WR * 128];                 \
+  __shared__ __attribute__((aligned(16))) uint8_t s_b0[16 * (AROWV)];             \
+  __shared__ __attribute__((aligned(16))) uint8_t s_b1[NB1_ * 16 * (AROWV) + 16]; \
+  __shared__ __attribute__((aligned(16))) uint8_t s_bsf0[16 * 8];                 \
+  __shared__ __attribute__((aligned(16))) uint8_t s_bsf1[NB1_ * 16 * 8 + 16];     \
+  __shared__ int s_src[16];                                                       \
+  __shared__ float s_rs[16];                                                      \
+  __shared__ float s_amax[4][16]
+#define DECODE_LDS_ARGS s_w0, s_w1, s_sc, s_b0, s_b1, s_bsf0, s_bsf1, s_src, s_rs, s_amax
+
+// activation bytes per row per chunk, and the staged row stride of an item
+template <int MODE>
+constexpr int decode_acb() { return MODE == 3 ? KC / 2 : MODE == 2 ? KC : 2 * KC; }
+template <int MODE, bool FC1>
+constexpr int decode_arow() { return decode_acb<MODE>() + ((MODE == 0 && FC1) ? 0 : 16); }
+
+// RING2: chunk buffers in pairs, so the next chunk's loads are issued right
+// after the chunk's barrier (two workgroups per CU, one barrier per chunk);
+// otherwise one set of buffers, refilled after a second barrier once every
+// wave has read its operands (three workgroups per CU).  Measured per kernel
+// on the decode16 geometry: the pair wins only where the MFMA phase is
+// longest (group16 FC1, 512 vs 545 us); elsewhere the extra workgroup per
+// CU wins (e.g. group16 FC2 268 vs 277 us, FP8 FC1 471 vs 486 us).
+template <int MODE, bool FC1>
+__global__ __launch_bounds__(256, (MODE == 0 && FC1) ? 2 : 3) void fc_decode_kernel(FcArgs a) {
+  DECODE_LDS((decode_arow<MODE, FC1>()), MODE == 0 && FC1);
+  const int tile = blockIdx.y;
+  if (tile >= a.ntiles[0]) return;
+  decode_item<MODE, FC1>(a, tile, blockIdx.x, DECODE_LDS_ARGS);
+}
+
+// The XCD (accelerator complex die) this wave runs on.
+__device__ __forceinline__ int xcc_id() {
+  unsigned v;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
+  return (int)(v & 0xFu);
+}
+
+// Longest wait of an FC2 item for its tile's FC1 items, in ticks of the
+// 100 MHz real-time counter (50 ms, far beyond any real wait).
+constexpr uint64_t kMaxWaitTicks = 5000000;
+
+// Single-launch decode: FC1 items, then FC2 items, of the tiles of this
+// workgroup's XCD (see DecodeSync).  Within an XCD the L2 is shared and the
+// vector L1 is per CU and write-through, so a store is visible to the other
+// CUs of the XCD once it has completed; the FC2 side invalidates its L1
+// before reading h.  No agent-scope release is needed (it would write back
+// the whole L2).
+template <int MODE>
+__global__ __launch_bounds__(256, 2) void fc_decode_fused_kernel(FcArgs a1, FcArgs a2, DecodeSync y) {
+  // (one set of arrays for both item kinds: FC1's pairs, the wider row stride)
+  DECODE_LDS((decode_arow<MODE, false>()), MODE == 0);
+  __shared__ int s_item;
+  // Every branch and loop bound below is wave-uniform (scalar), and the
+  // claim, the release and the wait are done by all of wave 0: with a
+  // per-lane condition (thread 0 only) around them, the compiler may route
+  // the other lanes straight back to the loop's barriers, past the claim,
+  // and the waves then no longer pass through the items together.
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int x = xcc_id() % y.nx;
+  const int ntiles = __builtin_amdgcn_readfirstlane(a1.ntiles[0]);
+  const int ntx = ntiles > x ? (ntiles - x + y.nx - 1) / y.nx : 0;
+  const int n1 = ntx * y.nblk1, n = n1 + ntx * y.nblk2;
+  // Items are claimed one ahead: the next claim's round trip runs under the
+  // current item.  A workgroup's next item always comes later in the queue
+  // than its current one, so an FC1 item held as a next item belongs to a
+  // workgroup whose current item is an FC1 item too (which never waits):
+  // every wait ends.
+  auto claim = [&]() __attribute__((always_inline)) {
+    // one atomic for the wave (lane 0 adds 1), the old value in every lane
+    return __hip_atomic_fetch_add(y.queue + x, lane == 0 ? 1 : 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  if (wave == 0) s_item = __builtin_amdgcn_readfirstlane(claim());
+  __syncthreads();
+  int it = __builtin_amdgcn_readfirstlane(s_item);
+  for (;;) {
+    __syncthreads();  // (every wave has read s_item)
+    if (it >= n) break;
+    int next = 0;
+    if (wave == 0) next = claim();
+    if (it < n1) {
+      const int lt = it / y.nblk1;
+      const int t = lt * y.nx + x;
+      decode_item<MODE, true>(a1, t, it - lt * y.nblk1, DECODE_LDS_ARGS);
+      // this wave's stores of h (and of its maxima) have completed
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (wave == 0)
+        __hip_atomic_fetch_add(y.done + t, lane == 0 ? 1 : 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      const int j = it - n1, lt = j / y.nblk2;
+      const int t = lt * y.nx + x;
+      if (wave == 0) {
+        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+        for (;;) {
+          const int d = __builtin_amdgcn_readfirstlane(
+              __hip_atomic_load(y.done + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+          if (d >= y.nblk1) break;
+          if (__builtin_amdgcn_s_memrealtime() - t0 > kMaxWaitTicks) {
+            __hip_atomic_fetch_add(y.err, lane == 0 ? 1 : 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(2);
+        }
+      }
+      __syncthreads();
+      // lines of h this CU's L1 may hold from before the wait
+      asm volatile("buffer_inv sc0" ::: "memory");
+      decode_item<MODE, false>(a2, t, j - lt * y.nblk2, DECODE_LDS_ARGS);
+    }
+    __syncthreads();  // (every wave is past the item: s_item may be rewritten)
+    if (wave == 0) s_item = __builtin_amdgcn_readfirstlane(next);
+    __syncthreads();
+    it = __builtin_amdgcn_readfirstlane(s_item);
+  }
+}
+
+template <int MODE>
+hipError_t launch_fused(const FcArgs& a1, const FcArgs& a2, const DecodeSync& y, hipStream_t s) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 256;
+  // two workgroups per CU, every one resident at once (three would not fit
+  // the registers of both item kinds without spilling)
+  const int grid = cus * 2;
+  hipLaunchKernelGGL((fc_decode_fused_kernel<MODE>), dim3(grid), dim3(256), 0, s, a1, a2, y);
+  return hipGetLastError();
+}
+
 template <int MODE, bool FC1>
 hipError_t launch_one(const FcArgs& a, int max_tiles, hipStream_t s) {
   const int nblk = FC1 ? a.I / 64 : a.H / 128;
@@ -522,6 +648,22 @@ hipError_t launch_fc_decode(const FcArgs& a, int mode, bool fc1, int max_tiles, 
   if (mode == 1) return launch_one<1, false>(a, max_tiles, s);
   if (mode == 2) return launch_one<2, false>(a, max_tiles, s);
   return launch_one<3, false>(a, max_tiles, s);
+}
+
+int xcd_count() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 32)
+    return 1;
+  return cus / 32 > 8 ? 8 : cus / 32;
+}
+
+hipError_t launch_fc_decode_fused(const FcArgs& a1, const FcArgs& a2, int mode, const DecodeSync& y,
+                                  hipStream_t s) {
+  if (mode == 0) return launch_fused<0>(a1, a2, y, s);
+  if (mode == 1) return launch_fused<1>(a1, a2, y, s);
+  if (mode == 2) return launch_fused<2>(a1, a2, y, s);
+  return launch_fused<3>(a1, a2, y, s);
 }
 
 }  // namespace moefp4

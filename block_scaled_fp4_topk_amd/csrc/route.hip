@@ -171,6 +171,7 @@ __device__ int finish_counts(int c, int E, int tile_m, int drops, int* s_tmp, in
     o.offsets[E] = valid_total;
     o.ntiles[0] = tiles_total;
     o.flags[0] = drops;
+    o.flags[1] = 0;  // synchronisation timeouts of the single-launch decode kernel
   }
   return valid_total;
 }

@@ -167,6 +167,28 @@ moefp4_status moe_fp4_forward(const moefp4_problem* p,
                               void* out, void* workspace, size_t ws_bytes,
                               hipStream_t stream);
 
+/* moe_fp4_forward with FC1 and FC2 in one persistent launch: the fused
+ * form the pages set beside the baseline grouped GEMM ([P1] the commit that
+ * updates the MegaMoE synthetic benchmark: baseline grouped GEMM and fused
+ * MegaMoE fed from the same raw source tensors; [P2] Context: the fused
+ * FP8xFP4 MegaMoE compute path).  Each expert tile's FC2 work waits, inside
+ * the launch, for that tile's FC1 work on the same XCD (per-tile counters in
+ * the workspace; h passes through the XCD's own L2).  Same arguments,
+ * workspace size, arithmetic and result as moe_fp4_forward (bit-identical
+ * output); runs only problems of the 16-row decode tiles (at most 16
+ * assignments per active expert) and returns EUNSUPPORTED with a message
+ * otherwise.  Slower than moe_fp4_forward on the measured decode shapes; it
+ * exists as the single-launch form, not as the default.  If a wait of the
+ * fused kernel ever exceeded its 50 ms limit, the workspace's second word is
+ * nonzero and the result is not valid. */
+moefp4_status moe_fp4_forward_fused(const moefp4_problem* p,
+                                    const void* x, const uint8_t* x_sf,
+                                    const int32_t* topk_ids, const float* topk_w,
+                                    const uint8_t* w13, const uint8_t* w13_sf, const float* w13_gs,
+                                    const uint8_t* w2, const uint8_t* w2_sf, const float* w2_gs,
+                                    void* out, void* workspace, size_t ws_bytes,
+                                    hipStream_t stream);
+
 /* moe_fp4_forward without a caller workspace, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving
  * loops, harnesses that forbid allocation): the workspace is a static device

@@ -29,7 +29,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert {"moe_fp4_forward", "moe_fp4_route", "fp4_requant_gran_k", "moe_fp4_workspace_bytes",
+    assert {"moe_fp4_forward", "moe_fp4_forward_fused", "moe_fp4_route", "fp4_requant_gran_k", "moe_fp4_workspace_bytes",
             "moe_fp4_quantize_act", "moe_fp4_quantize_act_fp4", "moe_fp4_prepare_gemm_weights",
             "moefp4_last_error", "moefp4_version"} <= set(names)
     for n in names:
@@ -115,6 +115,24 @@ def test_forward_rejects_before_launch(L):
     # T = 0 is a valid empty call
     p0 = P(T=0)
     assert L.moe_fp4_forward(ctypes.byref(p0), z, z, z, z, z, z, z, z, z, z, z, z, 0, z) == 0
+
+
+def test_forward_fused_rejects_before_launch(L):
+    """The single-launch forward validates like moe_fp4_forward and refuses
+    problems that do not run on the 16-row decode tiles, before any launch."""
+    z = ctypes.c_void_p(0)
+    f = ctypes.c_void_p(1 << 20)
+    p = P()
+    st = L.moe_fp4_forward_fused(ctypes.byref(p), z, z, z, z, z, z, z, z, z, z, z, z, 0, z)
+    assert st == m.EINVAL and b"non-NULL" in L.moefp4_last_error()
+    st = L.moe_fp4_forward_fused(ctypes.byref(p), f, z, f, f, f, f, z, f, f, z, f, z, 0, z)
+    assert st == m.EWORKSPACE
+    # prefill-shaped (64 assignments per expert on 128-row GEMM tiles): refused
+    pp = P(T=8192, top_k=8, E=256, gran_k=32, act_fmt=m.ACT_FP8_UE8M0_K32)
+    st = L.moe_fp4_forward_fused(ctypes.byref(pp), f, f, f, f, f, f, z, f, f, z, f, f, 1 << 40, z)
+    assert st == m.EUNSUPPORTED and b"decode tiles" in L.moefp4_last_error()
+    p0 = P(T=0)
+    assert L.moe_fp4_forward_fused(ctypes.byref(p0), z, z, z, z, z, z, z, z, z, z, z, z, 0, z) == 0
 
 
 def test_requant_rejects_before_launch(L):
