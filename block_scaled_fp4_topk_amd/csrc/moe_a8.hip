@@ -214,17 +214,29 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const int n = (blockIdx.y * 256 + threadIdx.x) * 4;
   if (t >= T || n >= H) return;
   float4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < k; ++j) {
-    const int s = slot_of[t * k + j];
-    if (s < 0) continue;
-    const float wj = w[t * k + j];
-    // Y is read once: non-temporal (whole 4 KB row pieces per workgroup)
-    typedef float f32x4 __attribute__((ext_vector_type(4)));
-    const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(y + (size_t)s * H + n));
-    acc.x += wj * v.x;
-    acc.y += wj * v.y;
-    acc.z += wj * v.z;
-    acc.w += wj * v.w;
+  // Y is read once: non-temporal (whole 4 KB row pieces per workgroup).  The
+  // rows of 8 picks are loaded before any is summed (8 loads in flight per
+  // lane instead of one), then summed in pick order.
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    f32x4 v[8];
+    float wj[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = j0 + u;
+      const int s = j < k ? slot_of[t * k + j] : -1;
+      wj[u] = s >= 0 ? w[t * k + j] : 0.f;
+      v[u] = s >= 0 ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(y + (size_t)s * H + n))
+                    : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (j0 + u >= k || slot_of[t * k + j0 + u] < 0) continue;
+      acc.x += wj[u] * v[u].x;
+      acc.y += wj[u] * v[u].y;
+      acc.z += wj[u] * v[u].z;
+      acc.w += wj[u] * v[u].w;
+    }
   }
   if (F32) {
     *reinterpret_cast<float4*>(static_cast<float*>(out) + (size_t)t * H + n) = acc;
