@@ -275,7 +275,7 @@ __device__ __forceinline__ void quantize_block32_fp4(const uint16_t* __restrict_
 // Workgroup b of nb quantises 32-element blocks b * 1024 + tid, then every
 // nb * 1024 further; FP4: MXFP4 (16 code bytes per block), else E4M3 (32).
 template <bool FP4>
-__device__ void quantize_rows_from(const uint16_t* __restrict__ x, long long T, int H,
+__device__ __forceinline__ void quantize_rows_from(const uint16_t* __restrict__ x, long long T, int H,
                                    uint8_t* __restrict__ xq, uint8_t* __restrict__ xsf, int b,
                                    int nb) {
   const long long nblk = T * (H / 32);
