@@ -107,6 +107,13 @@ moefp4_status plan(const moefp4_problem* p, Layout* L) {
                        T * H < (1ull << 31) &&
                        A * I < (1ull << 31) && I * H < (1ull << 31);
   L->nt = avg > 16.0 ? (gemm_ok ? 8 : 4) : 1;
+  // the decode kernels address an expert's weights and the fp16 rows of x
+  // with 32-bit offsets
+  if (L->nt == 1 && (I * H >= (1ull << 31) || (L->g16_a16 && T * H >= (1ull << 31))))
+    return fail(MOEFP4_EUNSUPPORTED,
+                "decode-shaped problem too large for the 16-row tiles: needs I*H and (16-bit activations with "
+                "group16 weights) T*H below 2^31, got I*H=%zu T*H=%zu",
+                I * H, T * H);
   if (p->w_layout == MOEFP4_W_GEMM && L->nt != 8)
     return fail(MOEFP4_EUNSUPPORTED,
                 "GEMM-layout weights are read by the prefill GEMM only (FP8 / FP4 activations, group32, H and "

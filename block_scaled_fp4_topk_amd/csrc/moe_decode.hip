@@ -46,6 +46,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <type_traits>
+
 namespace moefp4 {
 
 namespace {
@@ -53,6 +55,24 @@ namespace {
 constexpr int KC = 256;   // K elements per chunk
 constexpr int WR = 128;   // weight rows per workgroup
 constexpr int kNT = 2;    // cache policy of the weight / scale loads: non-temporal
+
+// f(integral_constant<int, i>) for i = 0 .. N - 1, unrolled
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void unroll_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    unroll_for<N, I + 1>(f);
+  }
+}
+
+// A wave-uniform pointer held as one scalar register pair, so that a load
+// from it plus a 32-bit per-lane offset is selected as one instruction with
+// a scalar base (rather than 64-bit vector adds of its parts per load).
+__device__ __forceinline__ const uint8_t* sbase(const uint8_t* p) {
+  uint64_t v = reinterpret_cast<uint64_t>(p);
+  asm volatile("" : "+s"(v));
+  return reinterpret_cast<const uint8_t*>(v);
+}
 
 __device__ __forceinline__ uint32_t dw(const uint4& v, int r) {
   return r == 0 ? v.x : r == 1 ? v.y : r == 2 ? v.z : v.w;
@@ -86,8 +106,11 @@ __device__ __forceinline__ void decode_item(const FcArgs& a, const int tile, con
   constexpr int SG = 128 / SCB;                        // chunks per scale group
   constexpr int RPC = WR / SG;                         // scale lines staged per chunk (16 or 8)
 
-  const int e = a.tiles[2 * tile], m0 = a.tiles[2 * tile + 1];
-  const int ne = a.counts[e], oe = a.offsets[e];
+  // (wave-uniform by construction; readfirstlane states it for the
+  // persistent kernel, whose item index the compiler cannot prove uniform)
+  const int e = __builtin_amdgcn_readfirstlane(a.tiles[2 * tile]);
+  const int m0 = __builtin_amdgcn_readfirstlane(a.tiles[2 * tile + 1]);
+  const int ne = __builtin_amdgcn_readfirstlane(a.counts[e]), oe = __builtin_amdgcn_readfirstlane(a.offsets[e]);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, q = lane >> 4;
@@ -110,17 +133,21 @@ __device__ __forceinline__ void decode_item(const FcArgs& a, const int tile, con
 
   // weight loads: instruction i of a wave covers rows 32 wave + 8 i .. + 8;
   // lane -> row + lane / 8, LDS slot lane % 8 holding the row's 16-byte
-  // segment (lane % 8) ^ (row % 8)
-  const uint8_t* wsrc[4];
+  // segment (lane % 8) ^ (row % 8).  Addresses are a wave-uniform base (the
+  // expert's weights plus the chunk) and a 32-bit per-lane offset (the
+  // forward rejects experts of 2 GB or more), so each load is one
+  // instruction with no 64-bit address arithmetic per chunk.
+  uint32_t woff[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int lr = 32 * wave + 8 * i + (lane >> 3);
-    wsrc[i] = wexp + (size_t)wrow(lr) * rowb + 16 * ((lane & 7) ^ (lr & 7));
+    woff[i] = (uint32_t)wrow(lr) * (uint32_t)rowb + 16u * ((lane & 7) ^ (lr & 7));
   }
   auto issue_w = [&](int c, uint8_t* sw) __attribute__((always_inline)) {
+    const uint8_t* base = sbase(wexp + (size_t)c * 128);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_global_load_lds(wsrc[i] + (size_t)c * 128, sw + (32 * wave + 8 * i) * 128, 16, 0, kNT);
+      __builtin_amdgcn_global_load_lds(base + woff[i], sw + (32 * wave + 8 * i) * 128, 16, 0, kNT);
   };
   // scale loads: this wave's rows [rb0, rb0 + nrows) of group g's 128-byte
   // lines, 16 bytes per lane (8 rows per instruction) when the scale rows
@@ -151,6 +178,25 @@ __device__ __forceinline__ void decode_item(const FcArgs& a, const int tile, con
       if (8 * wave < RPC) issue_sc(g, j * RPC + 8 * wave, 8);
     } else {
       issue_sc(g, j * RPC + wave * (RPC / 4), RPC / 4);
+    }
+  };
+  // The same for group16 scales (always 16-byte rows of lines, RPC = 16:
+  // waves 0 and 1 load 8 rows each): the lane's row of slice 0 and its
+  // swizzled segment are fixed per lane, slice j adds a wave-uniform row step.
+  const int sc_lr = 8 * wave + (lane >> 3);
+  const uint32_t sc_seg = 16u * ((lane & 7) ^ sc_swz(sc_lr));
+  const uint32_t sc_off = MODE == 0 ? (uint32_t)wrow(sc_lr) * (uint32_t)sb + sc_seg : 0u;
+  const bool sc_full = (sb & 127) == 0;  // every line whole: no per-lane check
+  auto issue_sc_slice0 = [&](int g, int j) __attribute__((always_inline)) {
+    if (wave < 2) {
+      int rstep = 16 * j;
+      if (FC1) {
+        const bool up0 = a.w13_order != 0, upj = (j >= 4) != up0;
+        rstep = 16 * (j & 3) + (upj ? a.I : 0) - (up0 ? a.I : 0);
+      }
+      const uint8_t* base = sbase(sexp + (ptrdiff_t)rstep * sb + 128 * g);
+      if (sc_full || 128 * g + (int)sc_seg < sb)
+        __builtin_amdgcn_global_load_lds(base + sc_off, &s_sc[(j * RPC + 8 * wave) * 128], 16, 0, kNT);
     }
   };
 
@@ -184,7 +230,9 @@ __device__ __forceinline__ void decode_item(const FcArgs& a, const int tile, con
   // past the tile's tokens are not issued; a row past them in a partly
   // valid pair repeats the tile's first token (its MFMA column is never
   // stored).
-  const uint8_t* adma_src[2] = {nullptr, nullptr};
+  // (32-bit per-lane offsets from a wave-uniform base: the forward rejects
+  // decode batches whose fp16 rows reach 2 GB)
+  uint32_t adma_off[2] = {0u, 0u};
   bool adma_on[2] = {false, false};
   if (ADMA) {
     const int nvr = min(16, ne - m0);
@@ -193,16 +241,16 @@ __device__ __forceinline__ void decode_item(const FcArgs& a, const int tile, con
       const int i = wave + 4 * u, row = 2 * i + (lane >> 5);
       adma_on[u] = 2 * i < nvr;
       const int src = s_src[row < nvr ? row : 0];
-      adma_src[u] = static_cast<const uint8_t*>(a.act) + (size_t)src * ((size_t)(K / KC) * ACB) +
-                    16 * ((lane & 31) ^ (row & 15));
+      adma_off[u] = (uint32_t)src * (uint32_t)((K / KC) * ACB) + 16u * ((lane & 31) ^ (row & 15));
     }
   }
   auto issue_a = [&](int c, uint8_t* sbuf) __attribute__((always_inline)) {
     if (ADMA) {
+      const uint8_t* base = sbase(static_cast<const uint8_t*>(a.act) + (size_t)c * ACB);
 #pragma unroll
       for (int u = 0; u < 2; ++u)
         if (adma_on[u])
-          __builtin_amdgcn_global_load_lds(adma_src[u] + (size_t)c * ACB, sbuf + (wave + 4 * u) * 1024, 16, 0, 0);
+          __builtin_amdgcn_global_load_lds(base + adma_off[u], sbuf + (wave + 4 * u) * 1024, 16, 0, 0);
     }
   };
 
@@ -234,10 +282,33 @@ __device__ __forceinline__ void decode_item(const FcArgs& a, const int tile, con
   const int lrow1 = FC1 ? 64 + wave * 16 + r16 : wave * 32 + 16 + r16;
   int obase = FC1 ? rb * 64 + wave * 16 : rb * 128 + wave * 32;
 
+  // LDS byte offsets of this lane's operand reads within a buffer, computed
+  // once (the empty asm makes them opaque, so the compiler keeps them in
+  // registers and puts the buffer's own address in each read's offset field
+  // instead of rebuilding every address each chunk)
+  uint32_t lw[4] = {(uint32_t)(lrow0 * 128 + 16 * ((2 * q) ^ (lrow0 & 7))),
+                    (uint32_t)(lrow0 * 128 + 16 * ((2 * q + 1) ^ (lrow0 & 7))),
+                    (uint32_t)(lrow1 * 128 + 16 * ((2 * q) ^ (lrow1 & 7))),
+                    (uint32_t)(lrow1 * 128 + 16 * ((2 * q + 1) ^ (lrow1 & 7)))};
+  asm volatile("" : "+v"(lw[0]), "+v"(lw[1]), "+v"(lw[2]), "+v"(lw[3]));
+  // activation reads: ADMA rows keep segment 8 q + jj of row r16 in slot
+  // (8 q + jj) ^ r16; staged rows are plain (segment 8 q + jj at 16 jj past
+  // 128 q)
+  uint32_t la[8];
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj)
+    la[jj] = (uint32_t)(r16 * AROW + (ADMA ? 16 * ((8 * q + jj) ^ r16) : 128 * q + 16 * jj));
+  if (ADMA)
+    asm volatile("" : "+v"(la[0]), "+v"(la[1]), "+v"(la[2]), "+v"(la[3]), "+v"(la[4]), "+v"(la[5]), "+v"(la[6]),
+                 "+v"(la[7]));
+  else
+    asm volatile("" : "+v"(la[0]));
+
   // the lane's weight-scale bytes of the current group, one entry per chunk
   // (group16: the 4 scales of K [64 q, 64 q + 64) for each of the two rows;
-  // group32: the 2 scales of each row, row 0 in the low half); consumed
-  // from entry 0 and shifted down each chunk
+  // group32: the 2 scales of each row, row 0 in the low half).  Group16
+  // chunks are unrolled over the group, so entry j is read by chunk j;
+  // otherwise the entries are consumed from 0 and shifted down each chunk.
   constexpr int NSR = MODE == 0 ? 2 * SG : SG;
   uint32_t sreg[NSR];
 #pragma unroll
@@ -252,9 +323,11 @@ __device__ __forceinline__ void decode_item(const FcArgs& a, const int tile, con
   v4f acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   // one chunk: its weights (sw) and activations (sb, sbsf) were loaded
   // during the previous chunk; RING2 loads the next chunk into the other
-  // buffers (sw_next)
-  auto step = [&](int c, const uint8_t* sw, uint8_t* sw_next, uint8_t* sb, uint8_t* sb_next, uint8_t* sbsf)
-      __attribute__((always_inline)) {
+  // buffers (sw_next).  JJ: integral_constant of the chunk's index in its
+  // scale group g (group16), or -1 (index taken from c at run time)
+  auto step = [&](auto JJ, int g, int c, const uint8_t* sw, uint8_t* sw_next, uint8_t* sb, uint8_t* sb_next,
+                  uint8_t* sbsf) __attribute__((always_inline)) {
+    constexpr int JS = decltype(JJ)::value;
     // stage chunk c's activations
     if (!ADMA && ssrc >= 0) {
       uint4 v0 = av0, v1 = av1;
@@ -281,7 +354,7 @@ __device__ __forceinline__ void decode_item(const FcArgs& a, const int tile, con
     // the last group start may be refilled
     __syncthreads();
 
-    const int j = c % SG;
+    const int j = JS >= 0 ? JS : c % SG;
     if (j == 0) {
       // a new scale group: this lane's scales of all its chunks
       const int x0 = 4 * sc_swz(lrow0), x1 = 4 * sc_swz(lrow1);
@@ -300,11 +373,17 @@ __device__ __forceinline__ void decode_item(const FcArgs& a, const int tile, con
         }
       }
     }
-    const uint32_t s0 = MODE == 0 ? sreg[0] : (sreg[0] & 0xFFFFu);
-    const uint32_t s1 = MODE == 0 ? sreg[1] : (sreg[0] >> 16);
-    constexpr int SSH = MODE == 0 ? 2 : 1;
+    uint32_t s0, s1;
+    if constexpr (JS >= 0) {
+      s0 = MODE == 0 ? sreg[2 * JS] : (sreg[JS] & 0xFFFFu);
+      s1 = MODE == 0 ? sreg[2 * JS + 1] : (sreg[JS] >> 16);
+    } else {
+      s0 = MODE == 0 ? sreg[0] : (sreg[0] & 0xFFFFu);
+      s1 = MODE == 0 ? sreg[1] : (sreg[0] >> 16);
+      constexpr int SSH = MODE == 0 ? 2 : 1;
 #pragma unroll
-    for (int i = 0; i + SSH < NSR; ++i) sreg[i] = sreg[i + SSH];
+      for (int i = 0; i + SSH < NSR; ++i) sreg[i] = sreg[i + SSH];
+    }
 
     // RING2: the next chunk's loads now.  The next group's scale lines
     // arrive a slice per chunk from the group's second chunk on (the group
@@ -316,17 +395,22 @@ __device__ __forceinline__ void decode_item(const FcArgs& a, const int tile, con
         issue_a(c + 1, sb_next);
         issue_w(c + 1, sw_next);
       }
-      if (c / SG + 1 < ngroups && j > 0) {
-        issue_sc_slice(c / SG + 1, j - 1);
-        if (j == SG - 1) issue_sc_slice(c / SG + 1, SG - 1);
+      if (g + 1 < ngroups && j > 0) {
+        if (MODE == 0) {
+          issue_sc_slice0(g + 1, j - 1);
+          if (j == SG - 1) issue_sc_slice0(g + 1, SG - 1);
+        } else {
+          issue_sc_slice(g + 1, j - 1);
+          if (j == SG - 1) issue_sc_slice(g + 1, SG - 1);
+        }
       }
     }
 
     // this chunk's operands, then its MFMAs
-    const uint4 w0a = *reinterpret_cast<const uint4*>(sw + lrow0 * 128 + 16 * ((2 * q) ^ (lrow0 & 7)));
-    const uint4 w0b = *reinterpret_cast<const uint4*>(sw + lrow0 * 128 + 16 * ((2 * q + 1) ^ (lrow0 & 7)));
-    const uint4 w1a = *reinterpret_cast<const uint4*>(sw + lrow1 * 128 + 16 * ((2 * q) ^ (lrow1 & 7)));
-    const uint4 w1b = *reinterpret_cast<const uint4*>(sw + lrow1 * 128 + 16 * ((2 * q + 1) ^ (lrow1 & 7)));
+    const uint4 w0a = *reinterpret_cast<const uint4*>(sw + lw[0]);
+    const uint4 w0b = *reinterpret_cast<const uint4*>(sw + lw[1]);
+    const uint4 w1a = *reinterpret_cast<const uint4*>(sw + lw[2]);
+    const uint4 w1b = *reinterpret_cast<const uint4*>(sw + lw[3]);
     const uint8_t* brow = sb + r16 * AROW;
     uint4 bv[8];
     int sbb0 = 0, sbb1 = 0;
@@ -346,12 +430,11 @@ __device__ __forceinline__ void decode_item(const FcArgs& a, const int tile, con
       sbb0 = (int)(sbb & 0xFFu);
       sbb1 = (int)(sbb >> 8);
     } else if (ADMA) {
-      // segment 8 q + jj of row r16 sits in slot (8 q + jj) ^ r16
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) bv[jj] = *reinterpret_cast<const uint4*>(brow + 16 * ((8 * q + jj) ^ r16));
+      for (int jj = 0; jj < 8; ++jj) bv[jj] = *reinterpret_cast<const uint4*>(sb + la[jj]);
     } else {
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) bv[jj] = *reinterpret_cast<const uint4*>(brow + 128 * q + 16 * jj);
+      for (int jj = 0; jj < 8; ++jj) bv[jj] = *reinterpret_cast<const uint4*>(sb + la[0] + 16 * jj);
     }
     if (!RING2) {
       __syncthreads();  // operands read: the buffers may be refilled
@@ -359,7 +442,10 @@ __device__ __forceinline__ void decode_item(const FcArgs& a, const int tile, con
         load_act(c + 1);
         issue_w(c + 1, s_w0);
       }
-      if (c / SG + 1 < ngroups) issue_sc_slice(c / SG + 1, j);
+      if (g + 1 < ngroups) {
+        if (MODE == 0) issue_sc_slice0(g + 1, j);
+        else issue_sc_slice(g + 1, j);
+      }
     }
     if (SCALED) {
 #pragma unroll
@@ -411,13 +497,29 @@ __device__ __forceinline__ void decode_item(const FcArgs& a, const int tile, con
       }
     }
   };
-  if (RING2) {
+  if constexpr (MODE == 0) {
+    // group16: the chunks of a scale group unrolled (SG = 8, even, so a
+    // chunk's RING2 buffer pair is fixed by its index in the group)
+    for (int g = 0; g < ngroups; ++g) {
+      unroll_for<SG>([&](auto J) __attribute__((always_inline)) {
+        constexpr int jc = decltype(J)::value;
+        const int c = g * SG + jc;
+        if (c < nchunks) {
+          if (RING2 && (jc & 1)) step(J, g, c, s_w1, s_w0, s_b1, s_b0, s_bsf1);
+          else if (RING2) step(J, g, c, s_w0, s_w1, s_b0, s_b1, s_bsf0);
+          else step(J, g, c, s_w0, s_w0, s_b0, s_b0, s_bsf0);
+        }
+      });
+    }
+  } else if (RING2) {
+    constexpr std::integral_constant<int, -1> JR{};
     for (int c = 0; c < nchunks; c += 2) {
-      step(c, s_w0, s_w1, s_b0, s_b1, s_bsf0);
-      if (c + 1 < nchunks) step(c + 1, s_w1, s_w0, s_b1, s_b0, s_bsf1);
+      step(JR, c / SG, c, s_w0, s_w1, s_b0, s_b1, s_bsf0);
+      if (c + 1 < nchunks) step(JR, (c + 1) / SG, c + 1, s_w1, s_w0, s_b1, s_b0, s_bsf1);
     }
   } else {
-    for (int c = 0; c < nchunks; ++c) step(c, s_w0, s_w0, s_b0, s_b0, s_bsf0);
+    constexpr std::integral_constant<int, -1> JR{};
+    for (int c = 0; c < nchunks; ++c) step(JR, c / SG, c, s_w0, s_w0, s_b0, s_b0, s_bsf0);
   }
 
   // epilogue: lane holds rows 4q..4q+3 of each 16-row tile, column r16
