@@ -92,6 +92,10 @@ def test_workspace_sizes(L):
     (dict(w_layout=1), m.EUNSUPPORTED),                                   # bf16 decode
     (dict(w_layout=1, gran_k=32, act_fmt=1), m.EUNSUPPORTED),             # FP8 decode (16-row tiles)
     (dict(w_layout=1, gran_k=32, act_fmt=1, T=8192, I=2304), m.EUNSUPPORTED),  # 64-row tiles
+    # the 16-row decode tiles address an expert's weights and the fp16 rows
+    # of x with 32-bit offsets
+    (dict(H=65536, I=32768), m.EUNSUPPORTED),                             # I*H = 2^31
+    (dict(T=8192, top_k=1, E=512, H=262144, I=256), m.EUNSUPPORTED),      # T*H = 2^31 (group16, bf16 x)
 ])
 def test_problem_validation(L, kw, status):
     st, _ = ws_status(P(**kw))
