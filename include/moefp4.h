@@ -154,7 +154,11 @@ moefp4_status moe_fp4_route(const moefp4_problem* p, const int32_t* topk_ids,
  * Supported: (BF16, gran 16), (BF16, gran 32), (FP8, gran 32), (FP4, gran
  * 32; H and I multiples of 512, the shapes of the FP8 / FP4 GEMM tiles).  FP8 or FP4 activations with group16 weights return
  * EUNSUPPORTED, like the capability gate on recipe (1, 1, 16) in [P1] / [P2]
- * Current patch scope.
+ * Current patch scope.  Decode-shaped problems (at most 16 assignments per
+ * active expert, run on 16-row tiles) need I*H below 2^31 and, for BF16
+ * activations with group16 weights, T*H below 2^31 (the decode kernels
+ * address an expert's weights and the fp16 copy of x with 32-bit offsets);
+ * EUNSUPPORTED otherwise.
  * x_sf must be NULL for BF16 and non-NULL for FP8 / FP4.  All pointers device
  * memory; topk_ids [T, k] int32, topk_w [T, k] float32; x, x_sf, the weight
  * and scale tensors and out 16-byte aligned, the workspace 256-byte aligned
