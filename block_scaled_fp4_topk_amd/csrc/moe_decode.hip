@@ -242,7 +242,7 @@ __device__ __forceinline__ void decode_item(const FcArgs& a, const int tile, con
   // past the tile's tokens are not issued, and in a partly valid pair the
   // lanes of the row past them load nothing (the row stays zero).
   // (32-bit per-lane offsets from a wave-uniform base: the forward rejects
-  // decode batches whose fp16 rows reach 2 GB)
+  // decode batches whose fp16 rows reach 4 GB)
   uint32_t adma_off[2] = {0u, 0u};
   bool adma_on[2] = {false, false};
   bool adma_row[2] = {false, false};  // this lane's row holds a token
