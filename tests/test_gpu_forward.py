@@ -54,7 +54,16 @@ SMALL = (combos(synth.CONFIGS["tiny"])
 # = 8 + 1), and scale rows that are not 16-byte multiples (group32: 136 and
 # 72 bytes)
 DECODE_LONG_K = combos(synth.variant(synth.CONFIGS["tiny"], T=16, E=8, k=4, H=4352, I=2304, seed=25))
-SMALL = SMALL + DECODE_LONG_K
+# the other lengths of a last scale group (group16: 8 chunks of 256 per
+# group, the group's chunks unrolled; FC1 with its paired buffers): FC1 13 =
+# 8 + 5 and 14 = 8 + 6 chunks, FC2 7 and 6
+DECODE_GROUP_TAILS = [
+    synth.variant(synth.CONFIGS["tiny"], T=16, E=8, k=4, H=3328, I=1792, seed=26, gran=16, act="bf16",
+                  global_scale="uniform"),
+    synth.variant(synth.CONFIGS["tiny"], T=12, E=8, k=3, H=3584, I=1536, seed=30, gran=16, act="bf16",
+                  global_scale="none"),
+]
+SMALL = SMALL + DECODE_LONG_K + DECODE_GROUP_TAILS
 
 
 @pytest.mark.parametrize("cfg", SMALL, ids=[_id(c) for c in SMALL])

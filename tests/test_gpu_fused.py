@@ -34,7 +34,10 @@ DECODE = (combos(synth.CONFIGS["tiny"])
           + combos(synth.variant(synth.CONFIGS["tiny"], T=16, E=32, k=4, H=1024, I=512, seed=21))
           + combos(synth.variant(synth.CONFIGS["tiny"], T=13, E=6, k=3, H=768, I=256, seed=22))
           + combos(synth.variant(synth.CONFIGS["tiny"], T=16, E=8, k=4, H=4352, I=2304, seed=25))
-          + combos(synth.variant(synth.CONFIGS["tiny"], T=1024, E=512, k=8, H=512, I=256, seed=43)))
+          + combos(synth.variant(synth.CONFIGS["tiny"], T=1024, E=512, k=8, H=512, I=256, seed=43))
+          # last scale groups of 5 (FC1) and 7 (FC2) group16 chunks
+          + [synth.variant(synth.CONFIGS["tiny"], T=16, E=8, k=4, H=3328, I=1792, seed=26, gran=16, act="bf16",
+                           global_scale="uniform")])
 
 
 def both(inp, d, order="gate_up", **kw):
