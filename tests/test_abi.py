@@ -216,3 +216,21 @@ def test_prepare_gemm_rejects_before_launch(L):
     assert pg(2, 1024, 512, 0, 0, ctypes.c_void_p((1 << 20) + 4), g, h, k, z) == m.EINVAL  # alignment
     assert pg(0, 1024, 512, 0, 0, z, z, z, z, z) == 0                    # empty
     assert len(L.moefp4_last_error()) == 0
+
+
+def test_measurement_helpers_validate_before_launch(L):
+    """The profiling hooks refuse bad arguments with a message and launch
+    nothing: the MFMA rate probe needs a sink and at least one iteration and
+    workgroup; the stage-event hook needs six events (NULL switches it off)."""
+    z = ctypes.c_void_p(0)
+    flops = ctypes.c_double(0.0)
+    probe = L.moefp4_mfma_peak_probe
+    assert probe(0, 0, 1, ctypes.c_void_p(1 << 20), ctypes.byref(flops), z) == m.EINVAL
+    assert probe(0, 1, 0, ctypes.c_void_p(1 << 20), ctypes.byref(flops), z) == m.EINVAL
+    assert probe(0, 1, 1, z, ctypes.byref(flops), z) == m.EINVAL
+    assert b"sink" in L.moefp4_last_error()
+    assert probe(1, 1, 1, ctypes.c_void_p(1 << 20), None, z) == m.EINVAL
+    events = (ctypes.c_void_p * 6)()
+    assert L.moefp4_set_stage_events(events, 5) == m.EINVAL
+    assert b"6" in L.moefp4_last_error()
+    assert L.moefp4_set_stage_events(None, 0) == 0
