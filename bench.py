@@ -33,6 +33,7 @@ METRIC = "FP4 MoE fwd tokens/s + achieved HBM GB/s (decode) / MFMA TFLOP/s (pref
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "fp8": 5000.0, "fp4": 10100.0}
 WORKLOAD_TEXT = {
+    "tiny": "tiny MoE: T=32 E=8 top-2 H=512 I=256, bf16 x, E2M1 + E4M3 k16, global scale 1 (latency only)",
     "decode16": "W4A16 NVFP4 decode: T=64 E=256 top-8 H=6144 I=2048, bf16 x, E2M1 + E4M3 k16 + fp32 global",
     "decode32": "FP8xFP4 decode: T=256 E=256 top-8 H=6144 I=2048, E4M3+UE8M0 k32 x, E2M1 + UE8M0 k32",
     "decode32_a4": "A4 decode: T=256 E=256 top-8 H=6144 I=2048, bf16 x quantised by the library to MXFP4 "
@@ -514,6 +515,20 @@ def gemm_counters(kernel_key, workload):
             if k in d}
 
 
+def tiny_latency(moe, torch, synth):
+    """The tiny MoE's forward: a latency, in microseconds (its few hundred
+    kilobytes and 50 MFLOP put no roofline in reach)."""
+    name = "tiny"
+    inp = synth.make_moe_inputs(workload_cfg(synth, name))
+    d = to_dev(torch, inp)
+    print(f"[bench] secondary {name}", file=sys.stderr, flush=True)
+    tm = run_forward_timed(moe, torch, inp, d, 50, 100)
+    del d
+    return {"workload": WORKLOAD_TEXT[name], "us_per_step": tm["wall_ms"] * 1e3,
+            "event_median_us": tm["event_median_ms"] * 1e3,
+            "stage_us": {k: v * 1e3 for k, v in tm["stage_ms"].items()}}
+
+
 def secondary(moe, torch, synth, args, inp16, d16, peaks):
     """The other workloads of the hot path, each timed the same way; the
     prefill ones with the MFMA roofline of their FC1 GEMM."""
@@ -521,6 +536,7 @@ def secondary(moe, torch, synth, args, inp16, d16, peaks):
     del d16
     torch.cuda.empty_cache()
     out["requant_layer"] = requant_layer(moe, torch, inp16)
+    out["tiny"] = tiny_latency(moe, torch, synth)
     for name in ("decode32", "decode32_a4", "decode16_fused", "decode32_fused", "prefill32", "prefill32_bf16q",
                  "prefill32_a4", "prefill32_prep", "prefill32_a4_prep"):
         cfg = workload_cfg(synth, name)
