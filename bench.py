@@ -286,18 +286,24 @@ def cpu_baseline(inp, budget_s=15.0):
     global _CPU_INP
     _CPU_INP = inp
     n = max(1, min(len(os.sched_getaffinity(0)), 16))
-    finished = []
+    finished, failed = [], []
     with mp.get_context("fork").Pool(n, initializer=_one_blas_thread) as pool:
         t0 = time.perf_counter()
         for t in range(inp.cfg.T):
-            pool.apply_async(_oracle_token, (t,), callback=lambda _: finished.append(time.perf_counter()))
+            pool.apply_async(_oracle_token, (t,), callback=lambda _: finished.append(time.perf_counter()),
+                             error_callback=failed.append)
         # until the budget is spent (and at least one token per worker, or
-        # every token, has finished)
-        while len(finished) < inp.cfg.T and (time.perf_counter() - t0 < budget_s
-                                             or len(finished) < min(n, inp.cfg.T)):
+        # every token, has finished); a worker's error ends the wait, and so
+        # does a hard limit of ten budgets
+        while (not failed and len(finished) < inp.cfg.T and time.perf_counter() - t0 < 10 * budget_s
+               and (time.perf_counter() - t0 < budget_s or len(finished) < min(n, inp.cfg.T))):
             time.sleep(0.05)
         ends = sorted(finished)
         pool.terminate()
+    if failed:
+        raise RuntimeError(f"the oracle baseline failed in a worker: {failed[0]!r}")
+    if not ends:
+        raise RuntimeError(f"the oracle baseline finished no token in {10 * budget_s:.0f} s")
     done, dt = len(ends), ends[-1] - t0
     _CPU_INP = None
     return {"value": done / dt, "unit": "tokens/s", "cores": n, "kind": "oracle",
