@@ -600,7 +600,7 @@ moefp4_status moefp4_mfma_peak_probe(int32_t a4, int32_t iters, int32_t blocks, 
                                      hipStream_t stream) {
   if (iters < 1 || blocks < 1 || !flops) return fail(MOEFP4_EINVAL, "iters, blocks >= 1 and flops non-NULL needed");
   if (!sink) return fail(MOEFP4_EINVAL, "sink must be non-NULL (blocks * 256 floats)");
-  *flops = (double)blocks * 4 * (double)iters * 32 * 2.0 * 16 * 16 * 128;
+  *flops = (double)blocks * 4 * (double)iters * 64 * 2.0 * 16 * 16 * 128;
   moefp4_status st = hip_status(moefp4::launch_mfma_peak(a4 != 0, iters, blocks, sink, stream), "mfma_peak");
   return st == MOEFP4_OK ? ok() : st;
 }

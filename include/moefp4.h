@@ -318,7 +318,8 @@ moefp4_status moefp4_set_stage_events(hipEvent_t* events, int32_t n);
  * loop of the block-scaled matrix instruction the prefill kernels issue
  * (v_mfma_scale_f32_16x16x128_f8f6f4; FP4 x FP8 operands, or FP4 x FP4 with
  * a4 != 0) on `blocks` workgroups of 4 waves (one per CU at a time), `iters`
- * x 32 instructions per wave, and writes the flop count it performs to *flops
+ * x 64 instructions per wave (64 independent accumulators, the prefill
+ * GEMM's stage), and writes the flop count it performs to *flops
  * (host); time it
  * with events on `stream` to get the instruction's delivered rate on this
  * GPU, the practical ceiling beside the published peak.  sink: device
