@@ -9,7 +9,8 @@ The default workload is the W4A16 NVFP4 group16 decode layer (T=64 tokens,
 E=256 experts, top-8, H=6144, I=2048).  Prints ONE JSON line with tokens/s,
 the HBM roofline of the dominant kernel (HIP events recorded by the library
 on the launch stream around each stage), the whole-forward roofline, the
-FP64 oracle timed on the host cores on a bounded sample (cpu_baseline), and
+FP64 oracle timed on the host cores on a bounded sample (cpu_baseline, and
+its group16 -> group32 requantisation as cpu_baseline_requant), and
 secondary figures for the other workloads of the hot path (FP8xFP4 decode,
 prefill, group16 -> group32 requantisation of the whole layer).
 """
@@ -312,6 +313,56 @@ def cpu_baseline(inp, budget_s=15.0):
                       f"{n} processes over tokens, one BLAS thread each"}
 
 
+_RQ_ROWS = 256  # rows of one expert's w13 per oracle requantisation task
+
+
+def _oracle_requant_slice(task):
+    e, r0 = task
+    inp = _CPU_INP
+    import oracle
+    oracle.requant_g16_to_g32(inp.w13[e:e + 1, r0:r0 + _RQ_ROWS], inp.w13_sf[e:e + 1, r0:r0 + _RQ_ROWS],
+                              None if inp.w13_gs is None else inp.w13_gs[e:e + 1])
+    return task
+
+
+def cpu_baseline_requant(inp, budget_s=5.0):
+    """The FP64 oracle's group16 -> group32 requantisation on this host's
+    cores, on a bounded sample of the layer: a process pool over slices of
+    256 rows of w13 (expert after expert, the same pool shape as
+    cpu_baseline) until about budget_s seconds; GB/s = the slices'
+    algorithmic bytes (codes and scales in, codes and scales out) / wall
+    time.  Runs before the GPU is initialised."""
+    import multiprocessing as mp
+    global _CPU_INP
+    _CPU_INP = inp
+    n = max(1, min(len(os.sched_getaffinity(0)), 16))
+    E, N, kh = inp.w13.shape
+    K = 2 * kh
+    tasks = [(e, r0) for e in range(E) for r0 in range(0, N - _RQ_ROWS + 1, _RQ_ROWS)]
+    finished, failed = [], []
+    with mp.get_context("fork").Pool(n, initializer=_one_blas_thread) as pool:
+        t0 = time.perf_counter()
+        for t in tasks[: 64 * n]:
+            pool.apply_async(_oracle_requant_slice, (t,), callback=lambda _: finished.append(time.perf_counter()),
+                             error_callback=failed.append)
+        while (not failed and len(finished) < min(len(tasks), 64 * n) and time.perf_counter() - t0 < 10 * budget_s
+               and (time.perf_counter() - t0 < budget_s or len(finished) < n)):
+            time.sleep(0.05)
+        ends = sorted(finished)
+        pool.terminate()
+    _CPU_INP = None
+    if failed:
+        raise RuntimeError(f"the oracle requantisation baseline failed in a worker: {failed[0]!r}")
+    if not ends:
+        raise RuntimeError(f"the oracle requantisation baseline finished no slice in {10 * budget_s:.0f} s")
+    done, dt = len(ends), ends[-1] - t0
+    per_slice = _RQ_ROWS * (K // 2 + K // 16 + K // 2 + K // 32)
+    return {"value": done * per_slice / dt / 1e9, "unit": "GB/s", "cores": n, "kind": "oracle",
+            "sample": f"{done} slices of {_RQ_ROWS} rows x K={K} of the decode16 layer's w13 "
+                      f"({done * per_slice / 1e6:.0f} MB algorithmic) in {dt:.1f} s; numpy FP64, a pool of {n} "
+                      f"processes over the slices, one BLAS thread each"}
+
+
 def measured_peaks(moe, torch):
     """What this GPU delivers, beside the published peaks: a 1 GiB device
     copy (read + write bytes / time) and the register-only loop of the
@@ -393,10 +444,12 @@ def main():
     cfg = workload_cfg(synth, args.workload)
     print(f"[bench] generating {cfg.name} inputs", file=sys.stderr, flush=True)
     inp = synth.make_moe_inputs(cfg)
-    cpu = None
+    cpu = cpu_rq = None
     if not args.no_cpu_baseline and not args.profile:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         cpu = cpu_baseline(inp)
+        if inp.cfg.gran == 16:
+            cpu_rq = cpu_baseline_requant(inp)
     moe.lib()  # fails loudly if the HIP library is not built
     d = to_dev(torch, inp)
     if cfg.name.endswith("_prep"):
@@ -445,6 +498,8 @@ def main():
         res["copy_calibration_bytes"] = copy_calibration(torch)
     if cpu is not None:
         res["cpu_baseline"] = cpu
+    if cpu_rq is not None:
+        res["cpu_baseline_requant"] = cpu_rq
     if not args.no_secondary and not args.profile:
         print("[bench] measured peaks", file=sys.stderr, flush=True)
         pk = measured_peaks(moe, torch)

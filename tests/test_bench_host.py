@@ -1,5 +1,6 @@
 """Host-side logic of bench.py that runs without a GPU: the oracle baseline's
-process pool (a bounded sample, one result per token) and its failure path
+process pools (a bounded sample, one result per token or per slice of
+requantised rows) and the failure path
 (an error in a worker ends the run with that error instead of waiting), the
 multi-GPU refusal, and the algorithmic byte count of the decode workload."""
 
@@ -29,6 +30,14 @@ def test_cpu_baseline_worker_error_is_raised(monkeypatch):
     monkeypatch.setattr(bench, "_oracle_token", broken)
     with pytest.raises(RuntimeError, match="failed in a worker"):
         bench.cpu_baseline(inp, budget_s=2.0)
+
+
+def test_cpu_baseline_requant_counts_bytes():
+    inp = synth.make_moe_inputs(synth.variant(synth.CONFIGS["decode16"], T=8, E=2))
+    r = bench.cpu_baseline_requant(inp, budget_s=1.0)
+    assert r["kind"] == "oracle" and r["unit"] == "GB/s" and r["value"] > 0
+    # every slice is 256 rows x K of codes and scales in and out
+    assert "256 rows x K=6144" in r["sample"]
 
 
 def test_more_than_one_gpu_is_refused():
