@@ -15,6 +15,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <algorithm>
+
 namespace moefp4 {
 
 namespace {
@@ -210,41 +212,48 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                                                       const int32_t* __restrict__ slot_of,
                                                       const float* __restrict__ w, int T, int k,
                                                       int H, void* __restrict__ out) {
-  const int t = blockIdx.x;
-  const int n = (blockIdx.y * 256 + threadIdx.x) * 4;
-  if (t >= T || n >= H) return;
-  float4 acc = {0.f, 0.f, 0.f, 0.f};
-  // Y is read once: non-temporal (whole 4 KB row pieces per workgroup).  The
-  // rows of 8 picks are loaded before any is summed (8 loads in flight per
-  // lane instead of one), then summed in pick order.
-  typedef float f32x4 __attribute__((ext_vector_type(4)));
-  for (int j0 = 0; j0 < k; j0 += 8) {
-    f32x4 v[8];
-    float wj[8];
+  // Work item b = (token t, column chunk c) in token-major order, so that
+  // consecutive workgroups read consecutive 4 KB pieces of the same Y rows;
+  // the grid strides over the items (it is capped below 2^32 work-items).
+  const int nch = (H / 4 + 255) / 256;
+  const long long items = (long long)T * nch;
+  for (long long b = blockIdx.x; b < items; b += gridDim.x) {
+    const int t = (int)(b / nch);
+    const int n = ((int)(b - (long long)t * nch) * 256 + threadIdx.x) * 4;
+    if (n >= H) continue;
+    float4 acc = {0.f, 0.f, 0.f, 0.f};
+    // Y is read once: non-temporal (whole 4 KB row pieces per workgroup).
+    // The rows of 8 picks are loaded before any is summed (8 loads in flight
+    // per lane instead of one), then summed in pick order.
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    for (int j0 = 0; j0 < k; j0 += 8) {
+      f32x4 v[8];
+      float wj[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int j = j0 + u;
-      const int s = j < k ? slot_of[t * k + j] : -1;
-      wj[u] = s >= 0 ? w[t * k + j] : 0.f;
-      v[u] = s >= 0 ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(y + (size_t)s * H + n))
-                    : f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+      for (int u = 0; u < 8; ++u) {
+        const int j = j0 + u;
+        const int s = j < k ? slot_of[(size_t)t * k + j] : -1;
+        wj[u] = s >= 0 ? w[(size_t)t * k + j] : 0.f;
+        v[u] = s >= 0 ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(y + (size_t)s * H + n))
+                      : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      if (j0 + u >= k || slot_of[t * k + j0 + u] < 0) continue;
-      acc.x += wj[u] * v[u].x;
-      acc.y += wj[u] * v[u].y;
-      acc.z += wj[u] * v[u].z;
-      acc.w += wj[u] * v[u].w;
+      for (int u = 0; u < 8; ++u) {
+        if (j0 + u >= k || slot_of[(size_t)t * k + j0 + u] < 0) continue;
+        acc.x += wj[u] * v[u].x;
+        acc.y += wj[u] * v[u].y;
+        acc.z += wj[u] * v[u].z;
+        acc.w += wj[u] * v[u].w;
+      }
     }
-  }
-  if (F32) {
-    *reinterpret_cast<float4*>(static_cast<float*>(out) + (size_t)t * H + n) = acc;
-  } else {
-    const uint32_t b0 = f32_to_bf16_rne(acc.x), b1 = f32_to_bf16_rne(acc.y);
-    const uint32_t b2 = f32_to_bf16_rne(acc.z), b3 = f32_to_bf16_rne(acc.w);
-    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + (size_t)t * H + n) =
-        uint2{b0 | (b1 << 16), b2 | (b3 << 16)};
+    if (F32) {
+      *reinterpret_cast<float4*>(static_cast<float*>(out) + (size_t)t * H + n) = acc;
+    } else {
+      const uint32_t b0 = f32_to_bf16_rne(acc.x), b1 = f32_to_bf16_rne(acc.y);
+      const uint32_t b2 = f32_to_bf16_rne(acc.z), b3 = f32_to_bf16_rne(acc.w);
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + (size_t)t * H + n) =
+          uint2{b0 | (b1 << 16), b2 | (b3 << 16)};
+    }
   }
 }
 
@@ -261,7 +270,9 @@ hipError_t launch_fc2_a8(const FcArgs& a, int max_tiles, hipStream_t s) {
 hipError_t launch_combine(const float* y, const int32_t* slot_of, const float* topk_w, int T,
                           int k, int H, void* out, bool out_f32, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  const dim3 grid(T, (H / 4 + 255) / 256);
+  // one workgroup per (token, column chunk), at most 2^22 (the kernel strides)
+  const long long items = (long long)T * ((H / 4 + 255) / 256);
+  const dim3 grid((unsigned)std::min<long long>(items, 1LL << 22));
   if (out_f32)
     hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(256), 0, s, y, slot_of, topk_w, T, k, H, out);
   else
