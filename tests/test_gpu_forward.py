@@ -63,7 +63,12 @@ DECODE_GROUP_TAILS = [
     synth.variant(synth.CONFIGS["tiny"], T=12, E=8, k=3, H=3584, I=1536, seed=30, gran=16, act="bf16",
                   global_scale="none"),
 ]
-SMALL = SMALL + DECODE_LONG_K + DECODE_GROUP_TAILS
+# the smallest shapes the forward takes (H = I = 256: one 256-K chunk in FC1
+# and FC2), on the 16-row decode tiles and (T = 300 over 2 experts) on the
+# 64-row tiles
+SMALLEST = (combos(synth.variant(synth.CONFIGS["tiny"], T=20, E=4, k=2, H=256, I=256, seed=27))
+            + combos(synth.variant(synth.CONFIGS["tiny"], T=300, E=2, k=2, H=256, I=256, seed=28)))
+SMALL = SMALL + DECODE_LONG_K + DECODE_GROUP_TAILS + SMALLEST
 
 
 @pytest.mark.parametrize("cfg", SMALL, ids=[_id(c) for c in SMALL])
