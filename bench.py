@@ -447,9 +447,17 @@ def main():
     cpu = cpu_rq = None
     if not args.no_cpu_baseline and not args.profile:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(inp)
+        # (a failure of the CPU baseline is reported in its place; the GPU
+        # measurement goes on)
+        try:
+            cpu = cpu_baseline(inp)
+        except Exception as e:  # noqa: BLE001
+            cpu = {"error": repr(e), "kind": "oracle"}
         if inp.cfg.gran == 16:
-            cpu_rq = cpu_baseline_requant(inp)
+            try:
+                cpu_rq = cpu_baseline_requant(inp)
+            except Exception as e:  # noqa: BLE001
+                cpu_rq = {"error": repr(e), "kind": "oracle"}
     moe.lib()  # fails loudly if the HIP library is not built
     d = to_dev(torch, inp)
     if cfg.name.endswith("_prep"):
